@@ -1,0 +1,305 @@
+"""Seeded synthetic inputs for paged-decode attention.
+
+This module only draws numbers and lays them out in memory: it holds none of
+the attention arithmetic, so the FP64 oracle (``oracle/``) and the HIP path
+(``paged_decode_attention_splitk_amd``) can both be fed from it without
+sharing any code with each other.
+
+Recipe (the same for every workload):
+
+1. ``rng = numpy.random.default_rng(seed)``.
+2. Sequence lengths: a fixed list, or ``rng.integers(lo, hi, n, endpoint=True)``
+   (inclusive integer uniform), then any forced lengths are written in.
+3. Block placement: every sequence needs ``ceil(L / block_size)`` blocks; the
+   pool holds their sum (or a fixed count); ``rng.permutation(pool_blocks)``
+   hands them out in sequence order, so block tables are a shuffle of the pool.
+4. Queries: ``rng.standard_normal((num_seqs, num_q_heads, head_dim), float32)``.
+5. K and V of sequence ``s`` come from ``default_rng([seed, s])``: one
+   ``standard_normal`` draw of shape ``(blocks, block_size, num_kv_heads,
+   head_dim)`` for K, then one for V.  A sequence can therefore be regenerated
+   on its own.
+6. FP32 -> BF16 by round-to-nearest-even on the bit pattern (NaN kept NaN).
+7. Token slots past the end of a sequence, and pool blocks no sequence owns,
+   hold a quiet-NaN canary in correctness runs (``canary=True``) and zeros
+   otherwise, so a kernel that reads masked memory into its arithmetic shows
+   up as NaN.  Block-table entries past a sequence's last block are -1.
+
+All arrays are numpy; BF16 data is held as ``uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+BF16_QNAN = np.uint16(0x7FC0)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round FP32 values to BF16 (nearest, ties to even) and return the bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    rounded = (u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16
+    out = rounded.astype(np.uint16)
+    out[nan] = BF16_QNAN
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen BF16 bit patterns to FP32 (exact).  A convenience for callers
+    that want to look at generated data; the oracle decodes on its own."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+# --------------------------------------------------------------------------
+# Workload definitions (shapes, length mixes, seeds)
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    seq_lens: tuple | None = None          # fixed lengths, or None to draw
+    len_range: tuple | None = None         # (lo, hi) inclusive
+    forced: tuple = ()                     # ((index, length), ...)
+    pool_blocks: int | None = None         # fixed pool size (else = total needed)
+    layout: str = "paged"                  # "paged" or "scratch"
+    tile_capacity: int = 0                 # tiled API only
+    description: str = ""
+
+
+WORKLOADS = {
+    "tiny": Workload(
+        name="tiny", seed=0, num_seqs=2, num_q_heads=8, num_kv_heads=2,
+        head_dim=128, block_size=16, seq_lens=(37, 100), pool_blocks=32,
+        description="2 seqs, lengths 37 and 100, 8 q / 2 kv heads, D 128, "
+                    "block 16, pool of 32 blocks, num_splits 1 and pinned 4"),
+    "batch": Workload(
+        name="batch", seed=1, num_seqs=32, num_q_heads=32, num_kv_heads=8,
+        head_dim=128, block_size=16, len_range=(512, 4096),
+        description="32 seqs, lengths U[512, 4096], 32 q / 8 kv heads, D 128, "
+                    "block 16, shuffled pool sized to the context, Auto on 256 CUs"),
+    "long": Workload(
+        name="long", seed=2, num_seqs=1, num_q_heads=24, num_kv_heads=4,
+        head_dim=128, block_size=16, seq_lens=(131072,),
+        description="1 seq of 131072 tokens, 24 q / 4 kv heads, D 128, block 16, "
+                    "Auto clamped to the split ceiling"),
+    "packed": Workload(
+        name="packed", seed=3, num_seqs=64, num_q_heads=32, num_kv_heads=4,
+        head_dim=256, block_size=16, len_range=(1024, 8192),
+        description="64 seqs, lengths U[1024, 8192], 32 q / 4 kv heads (pack "
+                    "width 8), D 256, block 16"),
+    "tiled": Workload(
+        name="tiled", seed=4, num_seqs=128, num_q_heads=16, num_kv_heads=4,
+        head_dim=256, block_size=32, len_range=(0, 16384),
+        forced=((0, 0), (1, 1), (2, 31), (3, 32), (4, 2048), (5, 16384), (127, 0)),
+        layout="scratch", tile_capacity=64,
+        description="128 seqs, lengths U[0, 16384] plus forced edge lengths, "
+                    "16 q / 4 kv heads, D 256, block 32, scratch-pool layout, "
+                    "64 blocks per tile"),
+}
+
+
+def draw_seq_lens(w: Workload) -> np.ndarray:
+    rng = np.random.default_rng(w.seed)
+    return _draw_lens(w, rng)
+
+
+def _draw_lens(w: Workload, rng) -> np.ndarray:
+    if w.seq_lens is not None:
+        lens = np.array(w.seq_lens, dtype=np.int64)
+    else:
+        lo, hi = w.len_range
+        lens = rng.integers(lo, hi, w.num_seqs, endpoint=True).astype(np.int64)
+    for idx, L in w.forced:
+        lens[idx] = L
+    assert lens.shape == (w.num_seqs,)
+    return lens
+
+
+# --------------------------------------------------------------------------
+# Generated inputs
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PagedInputs:
+    """One batch of paged-decode inputs (all host numpy arrays).
+
+    q            uint16 [num_seqs, num_q_heads, head_dim]            (BF16 bits)
+    k_cache      uint16 [num_blocks, block_size, num_kv_heads, head_dim]
+    v_cache      uint16 [num_blocks, block_size, num_kv_heads, head_dim]
+    block_tables int32  [num_seqs, max_blocks_per_seq]  (-1 = unused)
+    seq_lens     int32  [num_seqs]
+    scale        float  (an FP32 value)
+    """
+    workload: Workload
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_tables: np.ndarray
+    seq_lens: np.ndarray
+    scale: float
+
+    @property
+    def num_seqs(self): return self.q.shape[0]
+    @property
+    def num_q_heads(self): return self.q.shape[1]
+    @property
+    def head_dim(self): return self.q.shape[2]
+    @property
+    def num_kv_heads(self): return self.k_cache.shape[2]
+    @property
+    def block_size(self): return self.k_cache.shape[1]
+    @property
+    def num_blocks(self): return self.k_cache.shape[0]
+
+
+@dataclasses.dataclass
+class ScratchInputs:
+    """Inputs for the tiled step API with the scratch-pool slot layout
+    ``[slot, K|V, kv_head, block_size, head_dim]``.
+
+    q            uint16 [num_seqs, num_q_heads, head_dim]
+    pool         uint16 [num_slots, 2, num_kv_heads, block_size, head_dim]
+    slot_tables  int32  [num_seqs, max_blocks_per_seq]  (-1 = unused)
+    seq_lens     int32  [num_seqs]
+    """
+    workload: Workload
+    q: np.ndarray
+    pool: np.ndarray
+    slot_tables: np.ndarray
+    seq_lens: np.ndarray
+
+    @property
+    def num_seqs(self): return self.q.shape[0]
+    @property
+    def num_q_heads(self): return self.q.shape[1]
+    @property
+    def head_dim(self): return self.q.shape[2]
+    @property
+    def num_kv_heads(self): return self.pool.shape[2]
+    @property
+    def block_size(self): return self.pool.shape[3]
+    @property
+    def num_slots(self): return self.pool.shape[0]
+
+
+def _seq_kv(seed: int, s: int, nblk: int, bs: int, nkv: int, D: int):
+    r = np.random.default_rng([seed, s])
+    k = r.standard_normal((nblk, bs, nkv, D), dtype=np.float32)
+    v = r.standard_normal((nblk, bs, nkv, D), dtype=np.float32)
+    return f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+def _layout(w: Workload, rng, lens: np.ndarray, bs: int):
+    nblk = (lens + bs - 1) // bs
+    total = int(nblk.sum())
+    pool_blocks = total if w.pool_blocks is None else w.pool_blocks
+    if pool_blocks < total:
+        raise ValueError(f"pool of {pool_blocks} blocks cannot hold {total}")
+    perm = rng.permutation(pool_blocks)
+    max_blocks = max(1, int(nblk.max()) if len(nblk) else 1)
+    tables = np.full((len(lens), max_blocks), -1, dtype=np.int32)
+    off = 0
+    for s, n in enumerate(nblk):
+        tables[s, :n] = perm[off:off + n]
+        off += n
+    return nblk, pool_blocks, tables
+
+
+def make_paged(w: Workload | str, canary: bool = True, scale: float | None = None,
+               seq_lens=None) -> PagedInputs:
+    """Generate one paged-decode batch for workload ``w``.
+
+    ``seq_lens`` overrides the drawn lengths (the rest of the recipe is
+    unchanged) so edge cases can reuse a workload's shapes.
+    """
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    assert w.layout == "paged"
+    rng = np.random.default_rng(w.seed)
+    lens = _draw_lens(w, rng)
+    if seq_lens is not None:
+        lens = np.asarray(seq_lens, dtype=np.int64)
+        w = dataclasses.replace(w, num_seqs=len(lens), seq_lens=tuple(int(x) for x in lens),
+                                len_range=None, forced=())
+    bs, nkv, D, nq = w.block_size, w.num_kv_heads, w.head_dim, w.num_q_heads
+    nblk, pool_blocks, tables = _layout(w, rng, lens, bs)
+    q = f32_to_bf16_bits(rng.standard_normal((len(lens), nq, D), dtype=np.float32))
+    fill = BF16_QNAN if canary else np.uint16(0)
+    k_cache = np.full((pool_blocks, bs, nkv, D), fill, dtype=np.uint16)
+    v_cache = np.full((pool_blocks, bs, nkv, D), fill, dtype=np.uint16)
+
+    def one(s):
+        n = int(nblk[s])
+        if n == 0:
+            return
+        k, v = _seq_kv(w.seed, s, n, bs, nkv, D)
+        tail = int(lens[s]) - (n - 1) * bs          # valid slots of the last block
+        if canary and tail < bs:
+            k[n - 1, tail:] = BF16_QNAN
+            v[n - 1, tail:] = BF16_QNAN
+        ids = tables[s, :n]
+        k_cache[ids] = k
+        v_cache[ids] = v
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, range(len(lens))))
+    if scale is None:
+        scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    return PagedInputs(w, q, k_cache, v_cache, tables, lens.astype(np.int32), float(np.float32(scale)))
+
+
+def make_scratch(w: Workload | str, canary: bool = True, seq_lens=None) -> ScratchInputs:
+    """Generate inputs for the tiled API in the scratch-pool slot layout."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    assert w.layout == "scratch"
+    rng = np.random.default_rng(w.seed)
+    lens = _draw_lens(w, rng)
+    if seq_lens is not None:
+        lens = np.asarray(seq_lens, dtype=np.int64)
+        w = dataclasses.replace(w, num_seqs=len(lens), seq_lens=tuple(int(x) for x in lens),
+                                len_range=None, forced=())
+    bs, nkv, D, nq = w.block_size, w.num_kv_heads, w.head_dim, w.num_q_heads
+    nblk, pool_blocks, tables = _layout(w, rng, lens, bs)
+    q = f32_to_bf16_bits(rng.standard_normal((len(lens), nq, D), dtype=np.float32))
+    fill = BF16_QNAN if canary else np.uint16(0)
+    pool = np.full((max(pool_blocks, 1), 2, nkv, bs, D), fill, dtype=np.uint16)
+
+    def one(s):
+        n = int(nblk[s])
+        if n == 0:
+            return
+        k, v = _seq_kv(w.seed, s, n, bs, nkv, D)     # [n, bs, nkv, D]
+        tail = int(lens[s]) - (n - 1) * bs
+        if canary and tail < bs:
+            k[n - 1, tail:] = BF16_QNAN
+            v[n - 1, tail:] = BF16_QNAN
+        ids = tables[s, :n]
+        pool[ids, 0] = k.transpose(0, 2, 1, 3)
+        pool[ids, 1] = v.transpose(0, 2, 1, 3)
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, range(len(lens))))
+    return ScratchInputs(w, q, pool, tables, lens.astype(np.int32))
+
+
+def subset_paged(inp: PagedInputs, seqs) -> PagedInputs:
+    """The same pool with only the rows ``seqs`` of q / block_tables / seq_lens
+    (used to run a sequence alone against the very same memory)."""
+    seqs = np.asarray(seqs, dtype=np.int64)
+    return PagedInputs(inp.workload, np.ascontiguousarray(inp.q[seqs]), inp.k_cache, inp.v_cache,
+                       np.ascontiguousarray(inp.block_tables[seqs]),
+                       np.ascontiguousarray(inp.seq_lens[seqs]), inp.scale)
