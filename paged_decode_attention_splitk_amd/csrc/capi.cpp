@@ -1,0 +1,448 @@
+// C-ABI entry points: argument checks, kernel choice and launches.
+//
+// The one-shot call takes the problem statement's arguments (q, caches, block
+// tables, sequence lengths, scale, split count); the tiled handle follows the
+// "metrale_storage/tiled_attention.rs" page (TiledAttention: new / validate,
+// begin_step, step_tile, finalize, the public state buffers); "not
+// applicable" for the packed kernel mirrors that page set's convention of a
+// launcher that launches nothing and lets the caller run the other path.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "pda.h"
+#include "pda_geometry.h"
+#include "pda_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return PDA_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(PDA_EHIP_BASE - (int)e, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool head_dim_supported(uint32_t d) { return d == 64 || d == 128 || d == 256; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Head groups of one KV head: G q heads in groups of at most 8, as even as
+// possible.  Returns the group width; *hg receives the group count.
+int head_groups(uint32_t G, int* hg) {
+    const int groups = (int)((G + pda::kMaxHeadsPerGroup - 1) / pda::kMaxHeadsPerGroup);
+    *hg = groups;
+    return (int)((G + groups - 1) / groups);
+}
+
+// Waves per fold workgroup of a one-shot launch.  A pure function of the
+// shape and the split count (never of the batch), so a sequence's
+// reduction order, and its output bytes, do not depend on what it is
+// batched with.  Launches that give a single sequence few workgroups get
+// wider workgroups; LDS caps the width.
+int oneshot_waves(uint32_t nkv, int hg, uint32_t nsplit, uint32_t head_dim, int gc) {
+    const uint64_t per_seq = (uint64_t)nkv * hg * nsplit;
+    int w = per_seq >= 128 ? 4 : 8;
+    while (w > 1 && pda::fold_lds_bytes((int)head_dim, gc, w) > 64 * 1024) --w;
+    return w;
+}
+
+int tiled_waves(uint32_t head_dim, int gc) {
+    int w = 8;
+    while (w > 1 && pda::fold_lds_bytes((int)head_dim, gc, w) > 64 * 1024) --w;
+    return w;
+}
+
+struct DecodeShape {
+    uint32_t num_seqs, nq, nkv, D, bs, max_blocks, num_blocks;
+};
+
+int check_decode(const DecodeShape& s, const void* q, const void* k, const void* v,
+                 const int32_t* bt, const int32_t* lens, const void* out, bool need_out) {
+    if (s.num_seqs == 0) return PDA_OK;
+    if (!q || !k || !v || !bt || !lens || (need_out && !out))
+        return fail(PDA_EINVAL, "null pointer argument");
+    if (s.nkv == 0) return fail(PDA_EINVAL, "num_kv_heads is 0");
+    if (s.nq == 0 || s.nq % s.nkv != 0)
+        return fail(PDA_EINVAL, "num_q_heads (%u) is not a positive multiple of num_kv_heads (%u)",
+                    s.nq, s.nkv);
+    if (!head_dim_supported(s.D))
+        return fail(PDA_EINVAL, "head_dim %u not supported (64, 128 or 256)", s.D);
+    if (s.bs == 0 || s.bs % pda::kBlockQuantum != 0)
+        return fail(PDA_EINVAL, "block_size %u is not a positive multiple of %u", s.bs,
+                    pda::kBlockQuantum);
+    if (s.max_blocks == 0) return fail(PDA_EINVAL, "max_blocks_per_seq is 0");
+    if ((uint64_t)s.max_blocks * s.bs > 0x7FFFFFFFull)
+        return fail(PDA_EINVAL, "max_blocks_per_seq * block_size exceeds 2^31 - 1");
+    if (s.num_blocks == 0) return fail(PDA_EINVAL, "num_blocks is 0");
+    if ((uint64_t)s.bs * s.nkv * s.D > 0x7FFFFFFFull)
+        return fail(PDA_EINVAL, "one block exceeds 2^31 elements");
+    const size_t va = s.D == 64 ? 8 : 16;
+    if (!aligned(q, va) || !aligned(k, va) || !aligned(v, va) || (out && !aligned(out, 4)))
+        return fail(PDA_EINVAL, "q / k_cache / v_cache must be %zu-byte aligned", va);
+    if (!aligned(bt, 4) || !aligned(lens, 4))
+        return fail(PDA_EINVAL, "block_tables / seq_lens must be 4-byte aligned");
+    return PDA_OK;
+}
+
+pda::FoldParams fold_params(const DecodeShape& s, const void* q, const void* k, const void* v,
+                            const int32_t* bt, const int32_t* lens, int hg, float scale,
+                            uint32_t nsplit) {
+    pda::FoldParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.tables = bt;
+    p.lens = lens;
+    p.blk_s = (int64_t)s.bs * s.nkv * s.D;
+    p.tok_s = (int64_t)s.nkv * s.D;
+    p.kvh_s = (int64_t)s.D;
+    p.num_blocks = s.num_blocks;
+    p.nq = (int)s.nq;
+    p.nkv = (int)s.nkv;
+    p.G = (int)(s.nq / s.nkv);
+    p.HG = hg;
+    p.bs = (int)s.bs;
+    p.table_stride = (int)s.max_blocks;
+    p.nsplit = (int)nsplit;
+    p.c = scale * kLog2e;
+    return p;
+}
+
+int run_partials(const DecodeShape& s, const void* q, const void* k, const void* v,
+                 const int32_t* bt, const int32_t* lens, float* ws, uint64_t ws_floats,
+                 float scale, uint32_t nsplit, hipStream_t stream) {
+    if (!ws) return fail(PDA_EINVAL, "workspace is NULL with num_splits > 1");
+    if (!aligned(ws, 8)) return fail(PDA_EINVAL, "workspace must be 8-byte aligned");
+    const uint64_t need = pda_workspace_slots(s.num_seqs, s.nq, nsplit, s.D);
+    if (ws_floats < need)
+        return fail(PDA_EINVAL, "workspace holds %llu floats, needs %llu",
+                    (unsigned long long)ws_floats, (unsigned long long)need);
+    int hg = 0;
+    const int gc = head_groups(s.nq / s.nkv, &hg);
+    pda::FoldParams p = fold_params(s, q, k, v, bt, lens, hg, scale, nsplit);
+    p.ws = ws;
+    const int waves = oneshot_waves(s.nkv, hg, nsplit, s.D, gc);
+    const uint64_t gx = (uint64_t)s.nkv * hg * nsplit;
+    hipError_t e = pda::launch_fold(pda::kModePartial, (int)s.D, gc, p, (uint32_t)gx, s.num_seqs,
+                                    waves, stream);
+    if (e != hipSuccess) return hip_fail(e, "split-K partial launch");
+    return PDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pda_last_error(void) { return g_last_error.c_str(); }
+
+int pda_device_cu_count(int device, uint32_t* cu_count) {
+    if (!cu_count) return fail(PDA_EINVAL, "cu_count is NULL");
+    int n = 0;
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    *cu_count = (uint32_t)n;
+    return ok();
+}
+
+int pda_splitk_partials(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* seq_lens, float* workspace,
+                        uint64_t workspace_floats, uint32_t num_seqs, uint32_t num_q_heads,
+                        uint32_t num_kv_heads, uint32_t head_dim, uint32_t block_size,
+                        uint32_t max_blocks_per_seq, uint32_t num_blocks, float scale,
+                        uint32_t num_splits, void* stream) {
+    const DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, max_blocks_per_seq, num_blocks};
+    int rc = check_decode(s, q, k_cache, v_cache, block_tables, seq_lens, nullptr, false);
+    if (rc != PDA_OK) return rc;
+    if (num_splits < 2 || num_splits > pda::kMaxDecodeSplits)
+        return fail(PDA_EINVAL, "num_splits %u outside 2..%u for a partials launch", num_splits,
+                    pda::kMaxDecodeSplits);
+    if (!std::isfinite(scale)) return fail(PDA_EINVAL, "scale is not finite");
+    if (num_seqs == 0) return ok();
+    rc = run_partials(s, q, k_cache, v_cache, block_tables, seq_lens, workspace, workspace_floats,
+                      scale, num_splits, (hipStream_t)stream);
+    return rc == PDA_OK ? ok() : rc;
+}
+
+int pda_splitk_merge(const float* workspace, uint64_t workspace_floats, void* out,
+                     uint32_t num_seqs, uint32_t num_q_heads, uint32_t head_dim,
+                     uint32_t num_splits, void* stream) {
+    if (num_seqs == 0) return ok();
+    if (!workspace || !out) return fail(PDA_EINVAL, "null pointer argument");
+    if (!head_dim_supported(head_dim))
+        return fail(PDA_EINVAL, "head_dim %u not supported (64, 128 or 256)", head_dim);
+    if (num_q_heads == 0) return fail(PDA_EINVAL, "num_q_heads is 0");
+    if (num_splits < 1 || num_splits > pda::kMaxDecodeSplits)
+        return fail(PDA_EINVAL, "num_splits %u outside 1..%u", num_splits, pda::kMaxDecodeSplits);
+    if (!aligned(workspace, 8) || !aligned(out, 4))
+        return fail(PDA_EINVAL, "workspace must be 8-byte and out 4-byte aligned");
+    const uint64_t need = pda_workspace_slots(num_seqs, num_q_heads, num_splits, head_dim);
+    if (workspace_floats < need)
+        return fail(PDA_EINVAL, "workspace holds %llu floats, needs %llu",
+                    (unsigned long long)workspace_floats, (unsigned long long)need);
+    hipError_t e = pda::launch_merge(workspace, static_cast<uint16_t*>(out), num_seqs,
+                                     (int)num_q_heads, (int)head_dim, (int)num_splits,
+                                     (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "split-K merge launch");
+    return ok();
+}
+
+int pda_paged_decode(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                     float* workspace, uint64_t workspace_floats, uint32_t num_seqs,
+                     uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                     uint32_t block_size, uint32_t max_blocks_per_seq, uint32_t num_blocks,
+                     float scale, uint32_t num_splits, uint32_t flags, void* stream) {
+    const DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, max_blocks_per_seq, num_blocks};
+    int rc = check_decode(s, q, k_cache, v_cache, block_tables, seq_lens, out, true);
+    if (rc != PDA_OK) return rc;
+    if (flags & ~PDA_DECODE_PACKED) return fail(PDA_EINVAL, "unknown flags 0x%x", flags);
+    if (num_splits < 1 || num_splits > pda::kMaxDecodeSplits)
+        return fail(PDA_EINVAL, "num_splits %u outside 1..%u", num_splits, pda::kMaxDecodeSplits);
+    if (!std::isfinite(scale)) return fail(PDA_EINVAL, "scale is not finite");
+    hipStream_t st = (hipStream_t)stream;
+
+    if (flags & PDA_DECODE_PACKED) {
+        if (!pda_gqa_pack_shape_ok(num_q_heads, num_kv_heads, head_dim) || num_splits != 1) {
+            g_last_error = "packed kernel not applicable: needs num_q_heads == 8 * num_kv_heads, "
+                           "head_dim 256 and num_splits 1";
+            return PDA_NOT_APPLICABLE;
+        }
+        if (num_seqs == 0) return ok();
+        pda::PackedParams p{};
+        p.q = static_cast<const uint16_t*>(q);
+        p.k = static_cast<const uint16_t*>(k_cache);
+        p.v = static_cast<const uint16_t*>(v_cache);
+        p.tables = block_tables;
+        p.lens = seq_lens;
+        p.out = static_cast<uint16_t*>(out);
+        p.blk_s = (int64_t)block_size * num_kv_heads * head_dim;
+        p.tok_s = (int64_t)num_kv_heads * head_dim;
+        p.kvh_s = head_dim;
+        p.num_blocks = num_blocks;
+        p.nq = (int)num_q_heads;
+        p.nkv = (int)num_kv_heads;
+        p.bs = (int)block_size;
+        p.table_stride = (int)max_blocks_per_seq;
+        p.c = scale * kLog2e;
+        hipError_t e = pda::launch_packed(p, num_seqs, st);
+        if (e != hipSuccess) return hip_fail(e, "packed decode launch");
+        return ok();
+    }
+
+    if (num_seqs == 0) return ok();
+    if (num_splits == 1) {
+        int hg = 0;
+        const int gc = head_groups(num_q_heads / num_kv_heads, &hg);
+        pda::FoldParams p =
+            fold_params(s, q, k_cache, v_cache, block_tables, seq_lens, hg, scale, 1);
+        p.out = static_cast<uint16_t*>(out);
+        const int waves = oneshot_waves(num_kv_heads, hg, 1, head_dim, gc);
+        hipError_t e = pda::launch_fold(pda::kModeFinal, (int)head_dim, gc, p,
+                                        (uint32_t)(num_kv_heads * hg), num_seqs, waves, st);
+        if (e != hipSuccess) return hip_fail(e, "single-split decode launch");
+        return ok();
+    }
+    rc = run_partials(s, q, k_cache, v_cache, block_tables, seq_lens, workspace, workspace_floats,
+                      scale, num_splits, st);
+    if (rc != PDA_OK) return rc;
+    hipError_t e = pda::launch_merge(workspace, static_cast<uint16_t*>(out), num_seqs,
+                                     (int)num_q_heads, (int)head_dim, (int)num_splits, st);
+    if (e != hipSuccess) return hip_fail(e, "split-K merge launch");
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Tiled state API
+// ---------------------------------------------------------------------------
+
+}  // extern "C"
+
+struct pda_tiled {
+    pda_tiled_dims dims;
+    int device;
+    float* m;
+    float* l;
+    float* o;
+};
+
+extern "C" {
+
+int pda_tiled_validate(const pda_tiled_dims* d) {
+    if (!d) return fail(PDA_EINVAL, "dims is NULL");
+    if (d->num_kv_heads == 0) return fail(PDA_EINVAL, "num_kv_heads is 0");
+    if (d->num_q_heads % d->num_kv_heads != 0)
+        return fail(PDA_EINVAL, "num_q_heads (%u) is not a multiple of num_kv_heads (%u)",
+                    d->num_q_heads, d->num_kv_heads);
+    if (d->head_dim > pda::kMaxHeadDim)
+        return fail(PDA_EINVAL, "head_dim %u exceeds the maximum of %u", d->head_dim,
+                    pda::kMaxHeadDim);
+    if (!head_dim_supported(d->head_dim))
+        return fail(PDA_EINVAL, "head_dim %u not supported (64, 128 or 256)", d->head_dim);
+    if (d->num_q_heads == 0 || d->max_seqs == 0 || d->tile_capacity == 0)
+        return fail(PDA_EINVAL, "max_seqs, num_q_heads and tile_capacity must be positive");
+    if (d->block_size == 0 || d->block_size % pda::kBlockQuantum != 0)
+        return fail(PDA_EINVAL, "block_size %u is not a positive multiple of %u", d->block_size,
+                    pda::kBlockQuantum);
+    if ((uint64_t)d->tile_capacity * d->block_size > 0x7FFFFFFFull)
+        return fail(PDA_EINVAL, "tile_capacity * block_size exceeds 2^31 - 1");
+    return ok();
+}
+
+int pda_tiled_create(const pda_tiled_dims* d, pda_tiled** out) {
+    if (!out) return fail(PDA_EINVAL, "out is NULL");
+    int rc = pda_tiled_validate(d);
+    if (rc != PDA_OK) return rc;
+    pda_tiled* t = new (std::nothrow) pda_tiled{};
+    if (!t) return fail(PDA_ENOMEM, "handle allocation failed");
+    t->dims = *d;
+    hipError_t e = hipGetDevice(&t->device);
+    if (e != hipSuccess) {
+        delete t;
+        return hip_fail(e, "hipGetDevice");
+    }
+    const uint64_t slots = (uint64_t)d->max_seqs * d->num_q_heads;
+    e = hipMalloc((void**)&t->m, slots * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&t->l, slots * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc((void**)&t->o, slots * d->head_dim * sizeof(float));
+    if (e != hipSuccess) {
+        pda_tiled_destroy(t);
+        return e == hipErrorOutOfMemory ? fail(PDA_ENOMEM, "tiled state allocation failed")
+                                        : hip_fail(e, "hipMalloc");
+    }
+    *out = t;
+    return ok();
+}
+
+void pda_tiled_destroy(pda_tiled* t) {
+    if (!t) return;
+    if (t->m) (void)hipFree(t->m);
+    if (t->l) (void)hipFree(t->l);
+    if (t->o) (void)hipFree(t->o);
+    delete t;
+}
+
+int pda_tiled_get_dims(const pda_tiled* t, pda_tiled_dims* dims) {
+    if (!t || !dims) return fail(PDA_EINVAL, "null pointer argument");
+    *dims = t->dims;
+    return ok();
+}
+
+int pda_tiled_state(const pda_tiled* t, float** m, float** l, float** o) {
+    if (!t) return fail(PDA_EINVAL, "handle is NULL");
+    if (m) *m = t->m;
+    if (l) *l = t->l;
+    if (o) *o = t->o;
+    return ok();
+}
+
+int pda_tiled_begin_step(pda_tiled* t, uint32_t num_seqs, void* stream) {
+    if (!t) return fail(PDA_EINVAL, "handle is NULL");
+    if (num_seqs > t->dims.max_seqs)
+        return fail(PDA_EINVAL, "begin_step num_seqs %u > max_seqs %u", num_seqs,
+                    t->dims.max_seqs);
+    const uint64_t n_q = (uint64_t)num_seqs * t->dims.num_q_heads;
+    hipError_t e = pda::launch_tiled_begin(t->m, t->l, t->o, n_q, (int)t->dims.head_dim,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "begin_step launch");
+    return ok();
+}
+
+int pda_tiled_step_tile(pda_tiled* t, const void* q, const void* k_pool, const void* v_pool,
+                        uint64_t pool_blocks, const int32_t* tile_blocks,
+                        const int32_t* tile_block_counts, uint32_t num_seqs, int64_t blk_stride,
+                        int64_t tok_stride, int64_t kvh_stride, int32_t last_block_valid_slots,
+                        void* stream) {
+    if (!t) return fail(PDA_EINVAL, "handle is NULL");
+    const pda_tiled_dims& d = t->dims;
+    if (num_seqs > d.max_seqs)
+        return fail(PDA_EINVAL, "step_tile num_seqs %u > max_seqs %u", num_seqs, d.max_seqs);
+    if (num_seqs == 0) return ok();
+    if (!q || !k_pool || !v_pool || !tile_blocks || !tile_block_counts)
+        return fail(PDA_EINVAL, "null pointer argument");
+    if (last_block_valid_slots < 1 || (uint32_t)last_block_valid_slots > d.block_size)
+        return fail(PDA_EINVAL, "last_block_valid_slots %d outside 1..%u", last_block_valid_slots,
+                    d.block_size);
+    if (pool_blocks == 0 || pool_blocks > 0xFFFFFFFFull)
+        return fail(PDA_EINVAL, "pool_blocks must be in 1..2^32-1");
+    const size_t va = d.head_dim == 64 ? 8 : 16;
+    const int64_t se = (int64_t)(va / 2);
+    if (!aligned(q, va) || !aligned(k_pool, va) || !aligned(v_pool, va))
+        return fail(PDA_EINVAL, "q / pools must be %zu-byte aligned", va);
+    if (blk_stride < 0 || tok_stride < 0 || kvh_stride < 0 || blk_stride % se ||
+        tok_stride % se || kvh_stride % se)
+        return fail(PDA_EINVAL, "strides must be non-negative multiples of %lld elements",
+                    (long long)se);
+    if (tok_stride * (int64_t)d.block_size + d.head_dim > 0x7FFFFFFFll)
+        return fail(PDA_EINVAL, "tok_stride * block_size exceeds 2^31 - 1");
+    if (!aligned(tile_blocks, 4) || !aligned(tile_block_counts, 4))
+        return fail(PDA_EINVAL, "tile arrays must be 4-byte aligned");
+    int hg = 0;
+    const int gc = head_groups(d.num_q_heads / d.num_kv_heads, &hg);
+    pda::FoldParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k_pool);
+    p.v = static_cast<const uint16_t*>(v_pool);
+    p.tables = tile_blocks;
+    p.lens = tile_block_counts;
+    p.ws = t->m;
+    p.l_state = t->l;
+    p.o_state = t->o;
+    p.blk_s = blk_stride;
+    p.tok_s = tok_stride;
+    p.kvh_s = kvh_stride;
+    p.num_blocks = (uint32_t)pool_blocks;
+    p.nq = (int)d.num_q_heads;
+    p.nkv = (int)d.num_kv_heads;
+    p.G = (int)(d.num_q_heads / d.num_kv_heads);
+    p.HG = hg;
+    p.bs = (int)d.block_size;
+    p.table_stride = (int)d.tile_capacity;
+    p.nsplit = 1;
+    p.lbvs = last_block_valid_slots;
+    // the step takes no scale: 1 / sqrt(head_dim), rounded once to FP32
+    p.c = (float)(1.0 / std::sqrt((double)d.head_dim)) * kLog2e;
+    const int waves = tiled_waves(d.head_dim, gc);
+    hipError_t e = pda::launch_fold(pda::kModeTiled, (int)d.head_dim, gc, p,
+                                    (uint32_t)(d.num_kv_heads * hg), num_seqs, waves,
+                                    (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "step_tile launch");
+    return ok();
+}
+
+int pda_tiled_finalize(pda_tiled* t, void* out, uint32_t num_seqs, void* stream) {
+    if (!t) return fail(PDA_EINVAL, "handle is NULL");
+    if (num_seqs > t->dims.max_seqs)
+        return fail(PDA_EINVAL, "finalize num_seqs %u > max_seqs %u", num_seqs, t->dims.max_seqs);
+    if (num_seqs == 0) return ok();
+    if (!out || !aligned(out, 4)) return fail(PDA_EINVAL, "out is NULL or not 4-byte aligned");
+    const uint64_t n_q = (uint64_t)num_seqs * t->dims.num_q_heads;
+    hipError_t e = pda::launch_tiled_finalize(t->l, t->o, static_cast<uint16_t*>(out), n_q,
+                                              (int)t->dims.head_dim, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace pda {
+
+// What a fold launch writes.
+enum FoldMode : int {
+    kModePartial = 0,  // split-K partial (o, m, l) into the workspace
+    kModeFinal = 1,    // single split: BF16 o / l straight to the output
+    kModeTiled = 2,    // fold a tile into the persistent (m, l, o) state
+};
+
+// Arguments of one fold launch (passed by value as the kernel argument).
+struct FoldParams {
+    const uint16_t* q;       // bf16 [S, nq, D]
+    const uint16_t* k;       // bf16 K pool
+    const uint16_t* v;       // bf16 V pool
+    const int32_t* tables;   // block tables [S, table_stride] (one-shot) or
+                             // tile blocks [S, tile_capacity] (tiled)
+    const int32_t* lens;     // seq_lens [S] (one-shot) or tile block counts [S]
+    float* ws;               // workspace (partial) or m state (tiled)
+    float* l_state;          // tiled only
+    float* o_state;          // tiled only
+    uint16_t* out;           // final only: bf16 [S, nq, D]
+    int64_t blk_s, tok_s, kvh_s;   // element strides of the pools
+    uint32_t num_blocks;     // blocks in the pools; ids outside are dropped
+    int nq, nkv, G, HG;      // heads, GQA ratio, head groups per KV head
+    int bs, table_stride;
+    int nsplit;              // splits per sequence (one-shot)
+    int lbvs;                // valid slots of a tile's last block (tiled)
+    float c;                 // scale * log2(e)
+};
+
+// Heads one fold workgroup carries at most (the packed width).
+constexpr int kMaxHeadsPerGroup = 8;
+
+// LDS bytes a fold workgroup of `waves` waves needs.
+size_t fold_lds_bytes(int head_dim, int gc, int waves);
+
+// Launches the fold kernel for (mode, head_dim, gc) on grid x = `grid_x`,
+// y = number of sequences.  head_dim in {64, 128, 256}, gc in 1..8.
+hipError_t launch_fold(int mode, int head_dim, int gc, const FoldParams& p, uint32_t grid_x,
+                       uint32_t grid_y, int waves, hipStream_t stream);
+
+// Split-K merge: workspace -> bf16 out.
+hipError_t launch_merge(const float* ws, uint16_t* out, uint32_t num_seqs, int nq, int head_dim,
+                        int nsplit, hipStream_t stream);
+
+// Tiled state fill (m, l, o := -inf, 0, 0) and finalize.
+hipError_t launch_tiled_begin(float* m, float* l, float* o, uint64_t n_q, int head_dim,
+                              hipStream_t stream);
+hipError_t launch_tiled_finalize(const float* l, const float* o, uint16_t* out, uint64_t n_q,
+                                 int head_dim, hipStream_t stream);
+
+// GQA-packed MFMA decode (8 q heads x head_dim 256 per workgroup, one split).
+struct PackedParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* tables;
+    const int32_t* lens;
+    uint16_t* out;
+    int64_t blk_s, tok_s, kvh_s;
+    uint32_t num_blocks;
+    int nq, nkv;
+    int bs, table_stride;
+    float c;                 // scale * log2(e)
+};
+hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream);
+
+}  // namespace pda

@@ -9,3 +9,11 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP path through the C-ABI")
+
+
+def pytest_sessionstart(session):
+    # build the HIP library in-tree when it is missing (never rebuilds)
+    lib = os.path.join(ROOT, "paged_decode_attention_splitk_amd", "libpda.so")
+    if not os.path.exists(lib):
+        from paged_decode_attention_splitk_amd import _build
+        _build.build(verbose=True)

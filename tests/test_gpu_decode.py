@@ -1,0 +1,157 @@
+"""GPU parity of the one-shot paged decode (split-K kernel + merge) against
+the FP64 oracle, through the C ABI.  Needs an MI355X."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import workloads as W
+from oracle import attention as A
+from oracle import geometry as g
+from tests.gpu_util import (PagedOnDevice, assert_ml_close, assert_out_close, host_bf16,
+                            host_bits, say)
+
+import paged_decode_attention_splitk_amd as P
+
+CU = 256   # the workloads are stated for 256 compute units
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _check_partials(dev, ws, n):
+    inp = dev.inp
+    S, nq, D = inp.num_seqs, inp.num_q_heads, inp.head_dim
+    w = ws.cpu().numpy().reshape(S, nq, n, D + 2).astype(np.float64)
+    po, pm, pl = A.split_partials(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                                  inp.seq_lens, inp.scale, n)
+    assert_ml_close(w[..., D], pm, "workspace m")
+    assert_ml_close(w[..., D + 1], pl, "workspace l")
+    live = pl > 0
+    assert_out_close(w[..., :D][live] / w[..., D + 1][live][:, None],
+                     po[live] / pl[live][:, None], "workspace o / l")
+
+
+@pytest.mark.parametrize("n", [1, 4])
+def test_tiny_workload(n):
+    say(f"[tiny] splits={n}")
+    inp = W.make_paged("tiny", canary=True)        # NaN canaries in unused blocks and tails
+    dev = PagedOnDevice(inp)
+    rc, out, ws = dev.run(n)
+    assert rc == P.PDA_OK
+    ref, m, l = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                               inp.seq_lens, inp.scale)
+    assert_out_close(host_bf16(out), ref)
+    if n > 1:
+        _check_partials(dev, ws, n)
+
+
+def test_batch_workload_auto_full_size():
+    n = P.pda_auto_splits(CU, 32)
+    assert n == 16
+    say(f"[batch] splits={n} device CUs={P.pda_device_cu_count(0)}")
+    inp = W.make_paged("batch", canary=True)
+    dev = PagedOnDevice(inp)
+    rc, out, ws = dev.run(n)
+    ref, m, l = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                               inp.seq_lens, inp.scale)
+    assert_out_close(host_bf16(out), ref)
+    # workspace m / l of every split on four sequences
+    S, nq, D = inp.num_seqs, inp.num_q_heads, inp.head_dim
+    wsn = ws.cpu().numpy().reshape(S, nq, n, D + 2).astype(np.float64)
+    rows = [0, 7, 19, 31]
+    sub = W.subset_paged(inp, rows)
+    po, pm, pl = A.split_partials(sub.q, sub.k_cache, sub.v_cache, sub.block_tables,
+                                  sub.seq_lens, sub.scale, n)
+    assert_ml_close(wsn[rows][..., D], pm, "workspace m")
+    assert_ml_close(wsn[rows][..., D + 1], pl, "workspace l")
+    # the same call again gives the same bytes
+    _, out2, _ = dev.run(n)
+    assert np.array_equal(host_bits(out), host_bits(out2))
+
+
+def test_long_sequence_clamped_splits():
+    n = P.pda_auto_splits(CU, 24)
+    assert n == g.MAX_DECODE_SPLITS == 16
+    say(f"[long] splits={n}")
+    inp = W.make_paged("long", canary=True)
+    dev = PagedOnDevice(inp)
+    rc, out, ws = dev.run(n)
+    ref, m, l = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                               inp.seq_lens, inp.scale)
+    assert_out_close(host_bf16(out), ref)
+    _check_partials(dev, ws, n)
+
+
+@pytest.mark.parametrize("n", [1, 16])
+def test_packed_shape_unpacked_path(n):
+    say(f"[packed-shape unpacked] splits={n}")
+    inp = W.make_paged("packed", canary=True)
+    dev = PagedOnDevice(inp)
+    rc, out, ws = dev.run(n)
+    rows = [0, 1, 17, 40, 63]
+    sub = W.subset_paged(inp, rows)
+    ref, _, _ = A.paged_decode(sub.q, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens,
+                               sub.scale)
+    assert_out_close(host_bf16(out)[rows], ref)
+
+
+@pytest.mark.parametrize("lens", [(1, 1, 1), (0, 5, 0, 16), (15, 16, 17, 63, 64, 65, 1000)])
+def test_edge_lengths(lens):
+    say(f"[edge] lens={lens}")
+    base = W.Workload(name="edge", seed=7, num_seqs=len(lens), num_q_heads=8, num_kv_heads=2,
+                      head_dim=128, block_size=16, seq_lens=tuple(lens))
+    inp = W.make_paged(base, canary=True)
+    dev = PagedOnDevice(inp)
+    ref, _, _ = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
+                               inp.scale)
+    for n in (1, 3, 16):
+        rc, out, ws = dev.run(n)
+        got = host_bf16(out)
+        assert_out_close(got, ref, f"splits={n}")
+        for s, L in enumerate(lens):
+            if L == 0:
+                assert np.all(host_bits(out)[s] == 0)
+            if L == 1:
+                # one token: p = 1, l = 1, so out is v_0 exactly
+                blk = inp.block_tables[s, 0]
+                v0 = inp.v_cache[blk, 0]
+                G = inp.num_q_heads // inp.num_kv_heads
+                for h in range(inp.num_q_heads):
+                    assert np.array_equal(host_bits(out)[s, h], v0[h // G])
+
+
+@pytest.mark.parametrize("D,nq,nkv", [(64, 4, 4), (128, 6, 1), (256, 16, 2), (128, 40, 4)])
+def test_other_shapes(D, nq, nkv):
+    say(f"[shape] D={D} nq={nq} nkv={nkv}")
+    base = W.Workload(name="shape", seed=8, num_seqs=3, num_q_heads=nq, num_kv_heads=nkv,
+                      head_dim=D, block_size=32, seq_lens=(100, 700, 33))
+    inp = W.make_paged(base, canary=True, scale=0.07)
+    dev = PagedOnDevice(inp)
+    ref, _, _ = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
+                               inp.scale)
+    for n in (1, 5):
+        rc, out, ws = dev.run(n)
+        assert_out_close(host_bf16(out), ref, f"splits={n}")
+
+
+def test_batch_invariance_auto_and_pinned():
+    """Each sequence's output bytes are the same alone and co-batched with
+    127 others, under Auto and Pinned split counts."""
+    base = W.Workload(name="inv", seed=9, num_seqs=128, num_q_heads=32, num_kv_heads=8,
+                      head_dim=128, block_size=16, len_range=(1, 2048))
+    inp = W.make_paged(base, canary=True)
+    dev = PagedOnDevice(inp)
+    for n in (P.pda_num_splits(P.PDA_SPLITK_AUTO, 0, CU, 32, 128, 0),
+              P.pda_num_splits(P.PDA_SPLITK_PINNED, 5, CU, 32, 128, 0)):
+        say(f"[invariance] splits={n}")
+        _, out, _ = dev.run(n)
+        full = host_bits(out)
+        for s in range(128):
+            _, one, _ = dev.run(n, rows=[s])
+            assert np.array_equal(host_bits(one)[0], full[s]), f"seq {s} differs alone (n={n})"
