@@ -1,0 +1,255 @@
+"""Decode-step benchmark of the MI355X paged-decode attention library.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batch]
+
+A step is one whole decode pass over one batch: the split-K fold kernel
+(q.K^T, online softmax, P.V for every split) and the merge kernel, issued as
+the library's two C-ABI calls pda_splitk_partials + pda_splitk_merge (which
+is exactly what pda_paged_decode issues).  Inputs are resident in HBM before
+the timed region; the KV pool is held in several identical copies used in
+rotation, so no step finds its 301 MB of K/V in the 256 MB Infinity Cache
+left behind by the step before it.
+
+The default workload is batch decode: 32 sequences, lengths uniform in
+[512, 4096] (seed 1), 32 q / 8 kv heads, head_dim 128, block size 16, BF16
+N(0,1) data in a shuffled pool, split count from the Auto policy on 256 CUs
+(16).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+CU_COUNT = 256                 # the workloads are stated for 256 compute units
+METRIC = "decode-attention µs/step + achieved HBM GB/s (% of MI355X peak), 32 seqs × 4K ctx"
+FOLD_SRC = os.path.join(ROOT, "paged_decode_attention_splitk_amd", "csrc", "decode_fold.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fold_batch_traffic.json")
+
+
+def alg_bytes(inp, n_splits):
+    """Algorithmic HBM bytes of one decode step and of its two kernels.
+
+    fold:  K and V of every valid token (num_kv_heads * head_dim * 2 B each),
+           q, the block-table entries and lengths read, the workspace written;
+    merge: the workspace read, the BF16 output written.
+    """
+    import numpy as np
+    lens = inp.seq_lens.astype(np.int64)
+    S, nq, D = inp.q.shape
+    nkv, bs = inp.num_kv_heads, inp.block_size
+    kv = int(lens.sum()) * nkv * D * 2 * 2
+    q = S * nq * D * 2
+    tables = int(((lens + bs - 1) // bs).sum()) * 4 + S * 4
+    ws = S * nq * n_splits * (D + 2) * 4 if n_splits > 1 else 0
+    out = S * nq * D * 2
+    fold = kv + q + tables + ws
+    merge = ws + out
+    return {"kv": kv, "fold": fold, "merge": merge, "step": fold + merge}
+
+
+def _src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(per_launch_alg):
+    """HBM bytes per fold launch from the committed counter summary, or None
+    when missing or taken from a different kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("fold_source_sha256_16") != _src_hash(FOLD_SRC):
+        return None
+    return rec.get("fold_hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, seconds):
+    """The FP64 oracle on the host, one BLAS thread, repeated over the whole
+    batch until `seconds` have passed (at least once)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as A
+    reps, t0 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        while True:
+            A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
+                           inp.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return el / reps, reps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="batch")
+    ap.add_argument("--splits", type=int, default=0, help="pin a split count (default: Auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copies", type=int, default=0, help="KV pool copies (default: >= 1 GB)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(see the sharding note in DESIGN.md); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_decode_attention_splitk_amd as P
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev_cus = P.pda_device_cu_count(0)
+
+    inp = W.make_paged(args.workload, canary=False)
+    S, nq, D = inp.q.shape
+    nkv, bs = inp.num_kv_heads, inp.block_size
+    n = args.splits or P.pda_num_splits(P.PDA_SPLITK_AUTO, 0, CU_COUNT, nq, S, 0)
+    ab = alg_bytes(inp, n)
+    copies = args.copies or max(1, math.ceil(1.0e9 / ab["kv"]))
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    q = up(inp.q)
+    bt = torch.from_numpy(inp.block_tables).cuda()
+    lens = torch.from_numpy(inp.seq_lens).cuda()
+    ks = [up(inp.k_cache) for _ in range(copies)]
+    vs = [up(inp.v_cache) for _ in range(copies)]
+    wsf = P.pda_workspace_slots(S, nq, n, D)
+    ws = torch.empty(max(wsf, 1), dtype=torch.float32, device="cuda")
+    out = torch.empty((S, nq, D), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    mb = bt.shape[1]
+
+    def partials(i):
+        if n == 1:
+            P.pda_paged_decode(q, ks[i % copies], vs[i % copies], bt, lens, out, None, 0, S, nq,
+                               nkv, D, bs, mb, inp.num_blocks, inp.scale, 1, 0, sp)
+        else:
+            P.pda_splitk_partials(q, ks[i % copies], vs[i % copies], bt, lens, ws, wsf, S, nq,
+                                  nkv, D, bs, mb, inp.num_blocks, inp.scale, n, sp)
+
+    def merge():
+        if n > 1:
+            P.pda_splitk_merge(ws, wsf, out, S, nq, D, n, sp)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        partials(i)
+        merge()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    mid = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i].record(stream)
+        partials(i)
+        mid[i].record(stream)
+        merge()
+    ev[K].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / K
+    fold_ms = [ev[i].elapsed_time(mid[i]) for i in range(K)]
+    merge_ms = [mid[i].elapsed_time(ev[i + 1]) for i in range(K)]
+    gpu_ms = ev[0].elapsed_time(ev[K]) / K
+    fold_avg = float(np.mean(fold_ms))
+    merge_avg = float(np.mean(merge_ms))
+
+    # warm: the same pool every step (K/V partly served from the Infinity Cache)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(K):
+        partials(0)
+        merge()
+    torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - w0) * 1e3 / K
+
+    value = ab["step"] / (ms_per_step * 1e-3) / 1e9
+    achieved = ab["fold"] / (fold_avg * 1e-3) / 1e9
+    traffic = load_traffic(ab["fold"])
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": inp.workload.description,
+            "num_seqs": S, "num_q_heads": nq, "num_kv_heads": nkv, "head_dim": D,
+            "block_size": bs, "total_tokens": int(inp.seq_lens.sum()),
+            "seq_len_min": int(inp.seq_lens.min()), "seq_len_max": int(inp.seq_lens.max()),
+            "num_splits": n, "policy_cu_count": CU_COUNT, "device_cu_count": dev_cus,
+            "kv_pool_copies": copies, "algorithmic_bytes_per_step": ab["step"],
+        },
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "gpu_event_us_per_step": round(gpu_ms * 1e3, 2),
+        "warm_us_per_step": round(warm_ms * 1e3, 2),
+        "kernels_us": {"splitk_fold": round(fold_avg * 1e3, 2),
+                       "splitk_merge": round(merge_avg * 1e3, 2)},
+        "roofline": {
+            "kernel": "splitk fold (fold_kernel<0,128,4>)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": ab["fold"],
+        },
+    }
+    if not args.no_cpu:
+        sec, reps = cpu_baseline(inp, args.cpu_seconds)
+        rec["cpu_baseline"] = {
+            "value": round(ab["step"] / sec / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole {S}-sequence batch, FP64 numpy oracle with one BLAS thread, "
+                      f"{reps} repetition(s); {sec * 1e3:.1f} ms per step",
+            "ms_per_step": round(sec * 1e3, 2),
+        }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -60,9 +60,12 @@ int head_groups(uint32_t G, int* hg) {
 // reduction order, and its output bytes, do not depend on what it is
 // batched with.  Launches that give a single sequence few workgroups get
 // wider workgroups; LDS caps the width.
+#ifndef PDA_ONESHOT_WAVES_WIDE
+#define PDA_ONESHOT_WAVES_WIDE 4
+#endif
 int oneshot_waves(uint32_t nkv, int hg, uint32_t nsplit, uint32_t head_dim, int gc) {
     const uint64_t per_seq = (uint64_t)nkv * hg * nsplit;
-    int w = per_seq >= 128 ? 4 : 8;
+    int w = per_seq >= 128 ? PDA_ONESHOT_WAVES_WIDE : 8;
     while (w > 1 && pda::fold_lds_bytes((int)head_dim, gc, w) > 64 * 1024) --w;
     return w;
 }

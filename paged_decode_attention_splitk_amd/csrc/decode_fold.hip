@@ -9,25 +9,30 @@
 // [o[head_dim], m, l] FP32 slots follows the "Module attn_splitk" page
 // (MAX_DECODE_SPLITS, workspace_slots).
 //
-// Work layout inside a workgroup (W waves):
-//   * A K/V row of one token and one KV head is head_dim BF16 values.  LPT
-//     lanes share it (16 lanes for head_dim 64/128, 32 lanes for 256), each
-//     holding DPL = head_dim / LPT consecutive values, so one wave-wide
-//     vector load fetches ROWS = 64 / LPT token rows of 16-byte pieces.
-//   * Every lane keeps the q slices of all GC query heads of its KV head, so
-//     each K/V byte is read from HBM once and used by all GC heads straight
-//     from registers; no LDS staging is needed on the hot loop.
-//   * q.k is a chain of v_dot2_f32_bf16 over the lane's slice followed by a
-//     fixed DPP butterfly (quad xor 1, quad xor 2, half-row mirror, row
-//     mirror, and a permlane16 swap at 32 lanes), which leaves the same
-//     bits in every lane of the token row.
-//   * Each token row keeps its own (m, l, o) per head; tokens arrive in
-//     groups of TG = ROWS * U (one scalar block-table load per group), and a
-//     group updates the state once: new max, one rescale, U exponentials.
-//   * Waves take groups round-robin; at the end the rows of a wave are
-//     merged with permlane swaps and the waves through LDS, always in the
-//     same order, so the result depends only on the sequence's own data and
-//     the launch shape, never on the rest of the batch.
+// Work layout of a wave (the hot loop runs on VALU, so every step is laid
+// out to spend as few vector instructions per K/V byte as possible):
+//   * A K/V row of one token and one KV head is head_dim BF16 values; LPT =
+//     head_dim / 8 lanes share it, each holding one 16-byte piece, so one
+//     wave-wide buffer load fetches ROWS = 64 / LPT token rows.  A group is
+//     U such loads (TG = ROWS * U tokens, inside one block: one scalar
+//     block-table read per group).
+//   * Every lane keeps the q pieces of all GC query heads of its KV head, so
+//     each K/V byte is read from HBM once and serves all GC heads from
+//     registers.  q.k is a v_dot2_f32_bf16 chain over the piece: GC * U
+//     partial dots per lane.
+//   * The partial dots are transposed through LDS so that each lane owns
+//     whole (head, token) scores: one lane per score, so one exponential per
+//     score instead of one per score and lane, and no cross-lane butterfly.
+//     The U scores of a head sit in adjacent lanes; their max and sum are
+//     two DPP steps.  The probabilities and the per-head rescale factors go
+//     back through LDS to the lanes that hold V, which accumulate P.V in
+//     FP32.  LDS traffic never leaves the wave, so no barrier is needed.
+//   * The unnormalised o is rescaled only when some running max grew (the
+//     factor is exactly 1 otherwise, so skipping it changes no bit).
+//   * Each token row keeps its own state; at the end every (wave, row)
+//     state goes to LDS and one fixed-order pass merges them, so the result
+//     depends only on the sequence's own data and the launch shape, never
+//     on the rest of the batch.
 // Exponentials are v_exp_f32 (base 2): scores are scaled by scale * log2(e)
 // and m is converted back to natural-log units when it is stored.
 #include <hip/hip_runtime.h>
@@ -44,6 +49,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -65,89 +72,59 @@ __device__ __forceinline__ float dpp(float x) {
         __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Values of the even and the odd 16-lane row of this lane's row pair.
-__device__ __forceinline__ void rows16(float x, float& even, float& odd) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                              false);
-    even = __uint_as_float(r[0]);
-    odd = __uint_as_float(r[1]);
+// Max / sum over the N adjacent lanes (N = 2 or 4, aligned) holding the
+// scores of one head; every lane of the set gets identical bits.
+template <int N>
+__device__ __forceinline__ float nmax(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));                      // quad_perm [1,0,3,2]
+    if constexpr (N == 4) x = fmaxf(x, dpp<0x4E>(x));  // quad_perm [2,3,0,1]
+    return x;
 }
-// Values of the lower and the upper 32-lane half of the wave.
-__device__ __forceinline__ void rows32(float x, float& lo, float& hi) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                              false);
-    lo = __uint_as_float(r[0]);
-    hi = __uint_as_float(r[1]);
-}
-
-// Sum over the LPT lanes of a token row; every lane gets identical bits.
-template <int LPT>
-__device__ __forceinline__ float row_sum(float x) {
-    static_assert(LPT == 8 || LPT == 16 || LPT == 32, "lanes per token row");
-    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-    x += dpp<0x141>(x);  // row_half_mirror
-    if constexpr (LPT >= 16) x += dpp<0x140>(x);  // row_mirror
-    if constexpr (LPT >= 32) {
-        float e, o;
-        rows16(x, e, o);
-        x = e + o;
-    }
+template <int N>
+__device__ __forceinline__ float nsum(float x) {
+    x += dpp<0xB1>(x);
+    if constexpr (N == 4) x += dpp<0x4E>(x);
     return x;
 }
 
-template <int N>
-__device__ __forceinline__ void load_words(uint32_t (&d)[N], const uint16_t* p) {
-    static_assert(N == 2 || N == 4, "16- or 8-byte pieces");
-    if constexpr (N == 4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(p);
-        d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
-    } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(p);
-        d[0] = x.x; d[1] = x.y;
-    }
+// Orders this wave's LDS accesses: the writes before it are complete, and
+// visible to every lane of the wave, before the reads after it.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D>
+// Buffer descriptor over `bytes` bytes from `base` (raw, unswizzled; reads
+// past the range return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Lane layout of the fold for head_dim D and GC heads per workgroup.
+template <int D, int GC>
 struct FoldShape {
-    static constexpr int LPT = D == 256 ? 32 : 16;  // lanes per token row
-    static constexpr int DPL = D / LPT;             // values per lane
-    static constexpr int VEC = DPL / 2;             // 32-bit words per lane
-    static constexpr int ROWS = 64 / LPT;           // token rows per wave load
-    static constexpr int U = 4;                     // tokens per lane per group
-    static constexpr int TG = ROWS * U;             // tokens per group
+    static constexpr int LPT = D / 8;                 // lanes per token row
+    static constexpr int ROWS = 64 / LPT;             // token rows per wave load
+    static constexpr int U = ROWS == 8 ? 2 : 4;       // loads (tokens per lane) per group
+    static constexpr int TG = ROWS * U;                // tokens per group
+    static constexpr int NP = GC * U;                 // (head, token) scores per row
+    static constexpr int NP4 = (NP + 3) / 4 * 4;
+    static constexpr int PPL = (NP + LPT - 1) / LPT;  // scores a lane owns
+    static constexpr int TS = NP4 + 4;                // LDS floats per lane of partials
+    static constexpr int TROW = LPT * TS + 16;        // per token row (shifts the banks)
+    static constexpr int XS = (NP + GC + 3) / 4 * 4 + 4;  // exchange record per row
+    static constexpr int WAVE_FLOATS = ROWS * (TROW + XS);
     static_assert(kBlockQuantum % TG == 0, "a block holds whole groups");
+    static_assert(LPT % U == 0, "a head's scores sit in aligned lane sets");
 };
-
-// Merge the states of this lane's row with the partner row (XOR 16 or 32).
-template <int X, int GC, int DPL>
-__device__ __forceinline__ void merge_rows(float (&m)[GC], float (&l)[GC], float (&o)[GC][DPL]) {
-#pragma unroll
-    for (int h = 0; h < GC; ++h) {
-        float ma, mb, la, lb;
-        if constexpr (X == 16) { rows16(m[h], ma, mb); rows16(l[h], la, lb); }
-        else { rows32(m[h], ma, mb); rows32(l[h], la, lb); }
-        const float M = fmaxf(ma, mb);
-        const float Ms = M == kNegInf ? 0.f : M;
-        const float wa = fexp2(ma - Ms), wb = fexp2(mb - Ms);
-        m[h] = M;
-        l[h] = wa * la + wb * lb;
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) {
-            float oa, ob;
-            if constexpr (X == 16) rows16(o[h][d], oa, ob);
-            else rows32(o[h][d], oa, ob);
-            o[h][d] = wa * oa + wb * ob;
-        }
-    }
-}
 
 template <int MODE, int D, int GC>
 __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
-    using S = FoldShape<D>;
-    constexpr int LPT = S::LPT, DPL = S::DPL, VEC = S::VEC, ROWS = S::ROWS, U = S::U,
-                  TG = S::TG;
-    extern __shared__ float lds[];
+    using S = FoldShape<D, GC>;
+    constexpr int LPT = S::LPT, ROWS = S::ROWS, U = S::U, TG = S::TG, NP = S::NP,
+                  NP4 = S::NP4, PPL = S::PPL, TS = S::TS, TROW = S::TROW, XS = S::XS;
+    extern __shared__ __align__(16) float lds[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -180,33 +157,49 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
         t_end = (int64_t)t_begin + chunk < L ? t_begin + chunk : L;
     }
 
-    // q slices of the group's heads (zeros for heads past gcount).
-    uint32_t q2[GC][VEC];
+    // q pieces of the group's heads (zeros for heads past gcount).
+    uint32_t q2[GC][4];
 #pragma unroll
     for (int h = 0; h < GC; ++h) {
-        if (h < gcount) {
-            load_words(q2[h], p.q + ((int64_t)seq * p.nq + h0 + h) * D + sub * DPL);
-        } else {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (h < gcount)
+            w = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)seq * p.nq + h0 + h) * D +
+                                                sub * 8);
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) q2[h][j] = 0u;
-        }
+        for (int j = 0; j < 4; ++j) q2[h][j] = w[j];
     }
 
-    float m[GC], l[GC], o[GC][DPL];
+    // Row state: o for every head (this lane's 8 dims); m and l for the
+    // heads of the scores this lane owns (pair j = sub + LPT * k is head
+    // j / U, token j % U of the row).
+    float o[GC][8];
 #pragma unroll
-    for (int h = 0; h < GC; ++h) {
-        m[h] = kNegInf;
-        l[h] = 0.f;
+    for (int h = 0; h < GC; ++h)
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) o[h][d] = 0.f;
+        for (int d = 0; d < 8; ++d) o[h][d] = 0.f;
+    float m[PPL], l[PPL];
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+        m[k] = kNegInf;
+        l[k] = 0.f;
     }
 
-    const int gpb = p.bs / TG;  // groups per block
+    float* tw = lds + wave * S::WAVE_FLOATS;         // this wave's scratch
+    float* trow = tw + row * TROW;                   // partials of this row
+    float* xrow = tw + ROWS * TROW + row * XS;       // exchange record of this row
+
+    const int tok_b = (int)p.tok_s * 2;
+    uint32_t voff[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) voff[u] = (uint32_t)((row + ROWS * u) * tok_b + sub * 16);
+    const uint32_t voff0 = (uint32_t)(sub * 16);               // the group's first token
+    const uint32_t rec = (uint32_t)((p.bs - 1) * tok_b + D * 2);  // bytes a block spans
+
     // a live range starts on a block (hence group) boundary; an empty split
     // starts at the sequence end, which need not be aligned: it folds nothing
+    const int gpb = p.bs / TG;  // groups per block
     const int g_first = t_begin / TG;
     const int g_end = t_end > t_begin ? (t_end + TG - 1) / TG : g_first;
-    const int tok_s = (int)p.tok_s;
     const uint16_t* kh = p.k + (int64_t)kvh * p.kvh_s;
     const uint16_t* vh = p.v + (int64_t)kvh * p.kvh_s;
 
@@ -216,101 +209,146 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
         const int blk = blocks[b];
         if ((uint32_t)blk >= p.num_blocks) continue;  // dropped: never dereferenced
         const int nvalid = min(TG, t_end - g * TG);
-        const uint16_t* kb = kh + (int64_t)blk * p.blk_s;
-        const uint16_t* vb = vh + (int64_t)blk * p.blk_s;
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh + (int64_t)blk * p.blk_s, rec);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh + (int64_t)blk * p.blk_s, rec);
+        const int soff = slot0 * tok_b;
 
-        uint32_t kr[U][VEC], vr[U][VEC];
+        uint32_t kr[U][4], vr[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int r = row + ROWS * u;
             // a masked token re-reads the group's first row (always valid),
             // so canary memory past the end never enters the arithmetic
-            const int slot = slot0 + (r < nvalid ? r : 0);
-            const uint32_t off = (uint32_t)(slot * tok_s + sub * DPL);
-            load_words(kr[u], kb + off);
-            load_words(vr[u], vb + off);
-        }
-
-        float s[U][GC];
+            const uint32_t off = row + ROWS * u < nvalid ? voff[u] : voff0;
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, off, soff, 0);
+            const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, soff, 0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int h = 0; h < GC; ++h) {
-                float a = 0.f;
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) a = dot2(q2[h][j], kr[u][j], a);
-                s[u][h] = a;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bool ok = row + ROWS * u < nvalid;
-#pragma unroll
-            for (int h = 0; h < GC; ++h) {
-                const float a = row_sum<LPT>(s[u][h]);
-                s[u][h] = ok ? a * p.c : kNegInf;
+            for (int j = 0; j < 4; ++j) {
+                kr[u][j] = x[j];
+                vr[u][j] = y[j];
             }
         }
 
-        float vf[U][DPL];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                vf[u][2 * j] = bf_lo(vr[u][j]);
-                vf[u][2 * j + 1] = bf_hi(vr[u][j]);
-            }
-        }
-
-#pragma unroll
-        for (int h = 0; h < GC; ++h) {
-            float bm = s[0][h];
-#pragma unroll
-            for (int u = 1; u < U; ++u) bm = fmaxf(bm, s[u][h]);
-            const float mn = fmaxf(m[h], bm);
-            const float ms = mn == kNegInf ? 0.f : mn;
-            const float alpha = fexp2(m[h] - ms);
-            m[h] = mn;
-            float pu[U];
-            float lsum = alpha * l[h];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                pu[u] = fexp2(s[u][h] - ms);
-                lsum += pu[u];
-            }
-            l[h] = lsum;
-#pragma unroll
-            for (int d = 0; d < DPL; ++d) {
-                float acc = alpha * o[h][d];
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc = fmaf(pu[u], vf[u][d], acc);
-                o[h][d] = acc;
-            }
-        }
-    }
-
-    // Rows of the wave -> one state per wave (identical in every row).
-    if constexpr (ROWS >= 4) merge_rows<16, GC, DPL>(m, l, o);
-    if constexpr (ROWS >= 2) merge_rows<32, GC, DPL>(m, l, o);
-
-    // Waves -> LDS.  Layout: o [W][GC][D], m [W][GC], l [W][GC],
-    // weights [W + 1][GC], Lsum [GC].
-    float* lo_ = lds;
-    float* lm = lo_ + nw * GC * D;
-    float* ll = lm + nw * GC;
-    float* lw = ll + nw * GC;
-    float* lL = lw + (nw + 1) * GC;
-    if (row == 0) {
+        // partial dots of this lane's piece -> LDS, [row][lane][pair]
+        float part[NP4];
 #pragma unroll
         for (int h = 0; h < GC; ++h)
 #pragma unroll
-            for (int d = 0; d < DPL; ++d) lo_[(wave * GC + h) * D + sub * DPL + d] = o[h][d];
-    }
-    if (lane == 0) {
+            for (int u = 0; u < U; ++u) {
+                float a = 0.f;
 #pragma unroll
-        for (int h = 0; h < GC; ++h) {
-            lm[wave * GC + h] = m[h];
-            ll[wave * GC + h] = l[h];
+                for (int j = 0; j < 4; ++j) a = dot2(q2[h][j], kr[u][j], a);
+                part[h * U + u] = a;
+            }
+#pragma unroll
+        for (int j = NP; j < NP4; ++j) part[j] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NP4 / 4; ++c) {
+            const f32x4 w = {part[4 * c], part[4 * c + 1], part[4 * c + 2], part[4 * c + 3]};
+            *reinterpret_cast<f32x4*>(trow + sub * TS + 4 * c) = w;
+        }
+        wave_lds_sync();
+
+        // owned scores: sum the row's LPT partials in lane order
+        float sc[PPL];
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int j = sub + LPT * k;
+            float a = 0.f;
+            if (j < NP) {
+#pragma unroll
+                for (int jj = 0; jj < LPT; ++jj) a += trow[jj * TS + j];
+            }
+            const bool live = j < NP && row + ROWS * (j % U) < nvalid;
+            sc[k] = live ? a * p.c : kNegInf;
+        }
+
+        // per head: max over its U scores, new running max, p, l
+        float alpha[PPL];
+        bool grow = false;
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const float bm = nmax<U>(sc[k]);
+            const float mn = fmaxf(m[k], bm);
+            const float ms = mn == kNegInf ? 0.f : mn;
+            alpha[k] = fexp2(m[k] - ms);
+            grow |= mn != m[k];
+            m[k] = mn;
+            const float pk = fexp2(sc[k] - ms);
+            l[k] = l[k] * alpha[k] + nsum<U>(pk);
+            sc[k] = pk;
+        }
+
+        // probabilities and rescale factors back to every lane of the row
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int j = sub + LPT * k;
+            if (j < NP) {
+                xrow[j] = sc[k];
+                if (j % U == 0) xrow[NP + j / U] = alpha[k];
+            }
+        }
+        wave_lds_sync();
+        float pa[NP + GC];
+#pragma unroll
+        for (int c = 0; c < (NP + GC + 3) / 4; ++c) {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(xrow + 4 * c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * c + e < NP + GC) pa[4 * c + e] = w[e];
+        }
+
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int h = 0; h < GC; ++h) {
+                const float a = pa[NP + h];
+#pragma unroll
+                for (int d = 0; d < 8; ++d) o[h][d] *= a;
+            }
+        }
+
+        float vf[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                vf[u][2 * j] = bf_lo(vr[u][j]);
+                vf[u][2 * j + 1] = bf_hi(vr[u][j]);
+            }
+#pragma unroll
+        for (int h = 0; h < GC; ++h)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) {
+                float acc = o[h][d];
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc = fmaf(pa[h * U + u], vf[u][d], acc);
+                o[h][d] = acc;
+            }
+        wave_lds_sync();  // the next group's partials overwrite this scratch
+    }
+
+    // Every (wave, row) state -> LDS, then one fixed-order merge.  Layout
+    // (aliasing the loop scratch): o [NC][GC][D], m [NC][GC], l [NC][GC],
+    // weights [NC + 1][GC], L [GC], with NC = waves * ROWS contributors.
+    const int NC = nw * ROWS;
+    float* eo = lds;
+    float* em = eo + NC * GC * D;
+    float* el = em + NC * GC;
+    float* ew = el + NC * GC;
+    float* eL = ew + (NC + 1) * GC;
+    const int ci = wave * ROWS + row;
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < GC; ++h) {
+        float* dst = eo + (ci * GC + h) * D + sub * 8;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
+    }
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+        const int j = sub + LPT * k;
+        if (j < NP && j % U == 0) {
+            em[ci * GC + j / U] = m[k];
+            el[ci * GC + j / U] = l[k];
         }
     }
     __syncthreads();
@@ -326,20 +364,20 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
             m2_old = m_old * kLog2e;
             M = m2_old;
         }
-        for (int w = 0; w < nw; ++w) M = fmaxf(M, lm[w * GC + h]);
+        for (int c = 0; c < NC; ++c) M = fmaxf(M, em[c * GC + h]);
         const float Ms = M == kNegInf ? 0.f : M;
         float L = 0.f;
         if constexpr (MODE == kModeTiled) {
             const float wo = fexp2(m2_old - Ms);
-            lw[nw * GC + h] = wo;
+            ew[NC * GC + h] = wo;
             L = wo * l_old;
         }
-        for (int w = 0; w < nw; ++w) {
-            const float wt = fexp2(lm[w * GC + h] - Ms);
-            lw[w * GC + h] = wt;
-            L += wt * ll[w * GC + h];
+        for (int c = 0; c < NC; ++c) {
+            const float wt = fexp2(em[c * GC + h] - Ms);
+            ew[c * GC + h] = wt;
+            L += wt * el[c * GC + h];
         }
-        lL[h] = L;
+        eL[h] = L;
         const float m_nat = M * kLn2;
         if constexpr (MODE == kModePartial) {
             float* slot = p.ws + ((row_q + h) * p.nsplit + split) * (int64_t)(D + 2);
@@ -362,16 +400,17 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
         const int64_t qs = row_q + h;
         if constexpr (MODE == kModeTiled) {
             const float2 prev = *reinterpret_cast<const float2*>(p.o_state + qs * D + d);
-            const float wo = lw[nw * GC + h];
+            const float wo = ew[NC * GC + h];
             o0 = wo * prev.x;
             o1 = wo * prev.y;
         }
-        for (int w = 0; w < nw; ++w) {
-            const float wt = lw[w * GC + h];
-            o0 += wt * lo_[(w * GC + h) * D + d];
-            o1 += wt * lo_[(w * GC + h) * D + d + 1];
+        for (int c = 0; c < NC; ++c) {
+            const float wt = ew[c * GC + h];
+            const float2 x = *reinterpret_cast<const float2*>(eo + (c * GC + h) * D + d);
+            o0 += wt * x.x;
+            o1 += wt * x.y;
         }
-        const float L = lL[h];
+        const float L = eL[h];
         if constexpr (MODE == kModePartial) {
             if (L > 0.f) {
                 float* slot = p.ws + (qs * p.nsplit + split) * (int64_t)(D + 2);
@@ -387,44 +426,50 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
 }
 
 // Split-K merge: for each (sequence, q head), over splits in index order,
-// skipping splits with l == 0 (their o is never read):
+// skipping splits with l == 0 (their o is never used):
 //   M = max m_i,  w_i = exp(m_i - M),  L = sum w_i l_i,  O = sum w_i o_i,
 //   out = bf16(O / L), or 0 when every split is empty.
-// One wave per (sequence, head); lane j owns D/64 consecutive dims.
+// One wave per (sequence, head); lane j owns D/64 consecutive dims.  Every
+// split's (m, l) and o slice is requested before any is used, so the
+// wave waits for memory once, not once per split.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws,
                                                     uint16_t* __restrict__ out, int nq,
                                                     int nsplit) {
     constexpr int DPL = D / 64;
+    constexpr int NMAX = kMaxDecodeSplits;
     const int lane = threadIdx.x & 63;
-    const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int h = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (h >= nq) return;
     const int64_t qs = (int64_t)blockIdx.y * nq + h;
     const float* base = ws + qs * nsplit * (int64_t)(D + 2);
-    float M = kNegInf;
-    for (int i = 0; i < nsplit; ++i) {
-        const float li = base[i * (D + 2) + D + 1];
-        if (li > 0.f) M = fmaxf(M, base[i * (D + 2) + D]);
+    float mi[NMAX], li[NMAX], oi[NMAX][DPL];
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+        const int ii = i < nsplit ? i : nsplit - 1;   // re-read a valid slot
+        const float* slot = base + ii * (D + 2);
+        mi[i] = slot[D];
+        li[i] = slot[D + 1];
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) oi[i][d] = slot[lane * DPL + d];
     }
+    float M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < NMAX; ++i)
+        if (i < nsplit && li[i] > 0.f) M = fmaxf(M, mi[i]);
+    // selects rather than branches: every load above stays unconditional
+    // (so none is deferred into a branch), and a skipped split's o, which
+    // may be stale, never meets a multiply
     float L = 0.f, O[DPL];
 #pragma unroll
     for (int d = 0; d < DPL; ++d) O[d] = 0.f;
-    for (int i = 0; i < nsplit; ++i) {
-        const float* slot = base + i * (D + 2);
-        const float li = slot[D + 1];
-        if (!(li > 0.f)) continue;
-        const float w = fexp2((slot[D] - M) * kLog2e);
-        L += w * li;
-        if constexpr (DPL == 1) {
-            O[0] += w * slot[lane];
-        } else {
 #pragma unroll
-            for (int d = 0; d < DPL; d += 2) {
-                const float2 x = *reinterpret_cast<const float2*>(slot + lane * DPL + d);
-                O[d] += w * x.x;
-                O[d + 1] += w * x.y;
-            }
-        }
+    for (int i = 0; i < NMAX; ++i) {
+        const bool use = i < nsplit && li[i] > 0.f;
+        const float w = fexp2((mi[i] - M) * kLog2e);
+        L = use ? fmaf(w, li[i], L) : L;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) O[d] = use ? fmaf(w, oi[i][d], O[d]) : O[d];
     }
     uint16_t* dst = out + qs * D + lane * DPL;
     if constexpr (DPL == 1) {
@@ -499,11 +544,41 @@ FoldFn pick_d(int D, int gc) {
     }
 }
 
+template <int D, int GC>
+size_t fold_lds_floats(int waves) {
+    using S = FoldShape<D, GC>;
+    const size_t nc = (size_t)waves * S::ROWS;
+    const size_t epi = nc * GC * D + 2 * nc * GC + (nc + 1) * GC + GC;
+    const size_t loop = (size_t)waves * S::WAVE_FLOATS;
+    return epi > loop ? epi : loop;
+}
+
+template <int D>
+size_t lds_floats_d(int gc, int waves) {
+    switch (gc) {
+        case 1: return fold_lds_floats<D, 1>(waves);
+        case 2: return fold_lds_floats<D, 2>(waves);
+        case 3: return fold_lds_floats<D, 3>(waves);
+        case 4: return fold_lds_floats<D, 4>(waves);
+        case 5: return fold_lds_floats<D, 5>(waves);
+        case 6: return fold_lds_floats<D, 6>(waves);
+        case 7: return fold_lds_floats<D, 7>(waves);
+        case 8: return fold_lds_floats<D, 8>(waves);
+        default: return 0;
+    }
+}
+
 }  // namespace
 
 size_t fold_lds_bytes(int head_dim, int gc, int waves) {
-    return sizeof(float) * ((size_t)waves * gc * head_dim + 2 * (size_t)waves * gc +
-                            (size_t)(waves + 1) * gc + (size_t)gc);
+    size_t f = 0;
+    switch (head_dim) {
+        case 64: f = lds_floats_d<64>(gc, waves); break;
+        case 128: f = lds_floats_d<128>(gc, waves); break;
+        case 256: f = lds_floats_d<256>(gc, waves); break;
+        default: break;
+    }
+    return f * sizeof(float);
 }
 
 hipError_t launch_fold(int mode, int head_dim, int gc, const FoldParams& p, uint32_t grid_x,
