@@ -61,7 +61,7 @@ int head_groups(uint32_t G, int* hg) {
 // batched with.  Launches that give a single sequence few workgroups get
 // wider workgroups; LDS caps the width.
 #ifndef PDA_ONESHOT_WAVES_WIDE
-#define PDA_ONESHOT_WAVES_WIDE 4
+#define PDA_ONESHOT_WAVES_WIDE 2
 #endif
 int oneshot_waves(uint32_t nkv, int hg, uint32_t nsplit, uint32_t head_dim, int gc) {
     const uint64_t per_seq = (uint64_t)nkv * hg * nsplit;

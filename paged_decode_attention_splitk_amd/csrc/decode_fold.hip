@@ -101,6 +101,45 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              0x00020000);
 }
 
+// Sequences are folded longest first: blockIdx.y is a rank in descending
+// order of length (ties by index), so the hardware dispatcher, which hands
+// out workgroups in id order, schedules the longest work first and the grid
+// drains with short work items (longest-processing-time-first).  Only the
+// schedule changes; each item's arithmetic is the same in any order.  Every
+// wave ranks the lengths itself (a few scalar loads and compares), which is
+// cheap up to kRankMax sequences; larger batches keep their given order.
+constexpr int kRankMax = 256;
+
+__device__ __forceinline__ int clamp_len(int x, int cap) {
+    return x < 0 ? 0 : (x > cap ? cap : x);
+}
+
+#ifndef PDA_FOLD_LPT
+#define PDA_FOLD_LPT 1
+#endif
+__device__ int seq_of_rank(const int32_t* __restrict__ lens, int S, int r, int cap) {
+    if (!PDA_FOLD_LPT || S > kRankMax) return r;
+    const int lane = (int)__lane_id();
+    int found = -1;
+    for (int base = 0; base < S; base += 64) {
+        const int i = base + lane;
+        const int Li = i < S ? clamp_len(lens[i], cap) : -1;
+        int cnt = 0;
+        for (int j = 0; j < S; ++j) {
+            const int Lj = clamp_len(lens[j], cap);
+            cnt += (Lj > Li) | ((Lj == Li) & (j < i));
+        }
+        if (i < S && cnt == r) found = i;
+    }
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(found >= 0);
+    const int src = mask ? __builtin_ctzll(mask) : 0;
+    return __builtin_amdgcn_readlane(found, src);
+}
+
+#ifndef PDA_FOLD_PV_BF16
+#define PDA_FOLD_PV_BF16 0
+#endif
+
 // Lane layout of the fold for head_dim D and GC heads per workgroup.
 template <int D, int GC>
 struct FoldShape {
@@ -131,7 +170,8 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nw = blockDim.x >> 6;
     const int row = lane / LPT, sub = lane % LPT;
-    const int seq = blockIdx.y;
+    const int seq = seq_of_rank(p.lens, (int)gridDim.y, (int)blockIdx.y,
+                                MODE == kModeTiled ? p.table_stride : p.table_stride * p.bs);
     const int per_seq = p.nkv * p.HG;
     const int kvhg = MODE == kModeTiled ? (int)blockIdx.x : (int)blockIdx.x % per_seq;
     const int split = MODE == kModeTiled ? 0 : (int)blockIdx.x / per_seq;
@@ -155,6 +195,22 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
         const int64_t b0 = (int64_t)split * chunk;
         t_begin = b0 < L ? (int)b0 : L;
         t_end = (int64_t)t_begin + chunk < L ? t_begin + chunk : L;
+        if (t_begin >= t_end) {
+            // nothing to fold: an empty split leaves m = -inf, l = 0 (its o is
+            // never read); a single empty split is an all-zero output
+            const int64_t row_q0 = (int64_t)seq * p.nq + h0;
+            if constexpr (MODE == kModePartial) {
+                if (tid < gcount) {
+                    float* slot = p.ws + ((row_q0 + tid) * p.nsplit + split) * (int64_t)(D + 2);
+                    slot[D] = kNegInf;
+                    slot[D + 1] = 0.f;
+                }
+            } else {
+                for (int i = tid; i < gcount * (D / 2); i += blockDim.x)
+                    *reinterpret_cast<uint32_t*>(p.out + row_q0 * D + 2 * i) = 0u;
+            }
+            return;
+        }
     }
 
     // q pieces of the group's heads (zeros for heads past gcount).
@@ -306,6 +362,28 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
             }
         }
 
+#if PDA_FOLD_PV_BF16
+        // P.V on token pairs: v_dot2 of (p_a, p_b) as BF16 with the two
+        // tokens' values of one dim, accumulated in FP32
+#pragma unroll
+        for (int u = 0; u < U; u += 2) {
+            uint32_t vlo[4], vhi[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                vlo[j] = __builtin_amdgcn_perm(vr[u + 1][j], vr[u][j], 0x05040100u);
+                vhi[j] = __builtin_amdgcn_perm(vr[u + 1][j], vr[u][j], 0x07060302u);
+            }
+#pragma unroll
+            for (int h = 0; h < GC; ++h) {
+                const uint32_t pp = pack_bf16x2(pa[h * U + u], pa[h * U + u + 1]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    o[h][2 * j] = dot2(pp, vlo[j], o[h][2 * j]);
+                    o[h][2 * j + 1] = dot2(pp, vhi[j], o[h][2 * j + 1]);
+                }
+            }
+        }
+#else
         float vf[U][8];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -323,6 +401,7 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
                 for (int u = 0; u < U; ++u) acc = fmaf(pa[h * U + u], vf[u][d], acc);
                 o[h][d] = acc;
             }
+#endif
         wave_lds_sync();  // the next group's partials overwrite this scratch
     }
 
