@@ -167,34 +167,33 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    mid = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        ev[i].record(stream)
+
+    def timed(fn):
+        """Average ms of fn(i) over K calls, from HIP events on the launch
+        stream around the whole run, and the host wall clock of the run."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(K):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / K
+        return e0.elapsed_time(e1) / K, wall
+
+    def step(i):
         partials(i)
-        mid[i].record(stream)
         merge()
-    ev[K].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
 
-    ms_per_step = (t1 - t0) * 1e3 / K
-    fold_ms = [ev[i].elapsed_time(mid[i]) for i in range(K)]
-    merge_ms = [mid[i].elapsed_time(ev[i + 1]) for i in range(K)]
-    gpu_ms = ev[0].elapsed_time(ev[K]) / K
-    fold_avg = float(np.mean(fold_ms))
-    merge_avg = float(np.mean(merge_ms))
-
+    # the timed region: K whole decode steps
+    gpu_ms, ms_per_step = timed(step)
+    # each kernel on its own, back to back, for its average duration
+    fold_avg, _ = timed(partials)
+    merge_avg, _ = timed(lambda i: merge())
     # warm: the same pool every step (K/V partly served from the Infinity Cache)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for i in range(K):
-        partials(0)
-        merge()
-    torch.cuda.synchronize()
-    warm_ms = (time.perf_counter() - w0) * 1e3 / K
+    warm_ms, _ = timed(lambda i: (partials(0), merge()))
 
     value = ab["step"] / (ms_per_step * 1e-3) / 1e9
     achieved = ab["fold"] / (fold_avg * 1e-3) / 1e9
