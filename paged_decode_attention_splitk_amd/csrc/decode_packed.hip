@@ -1,12 +1,286 @@
-// GQA-packed decode kernel (placeholder until the MFMA kernel lands).
+// GQA-packed paged decode on MFMA (gfx950): one workgroup per (sequence, KV
+// head) carries that KV head's 8 query heads at head_dim 256 ("Module
+// attn_splitk" page: gqa_pack_shape_ok, gqa_pack_ctas, DECODE_GQA_PACK_*),
+// and is used only for single-split launches.  The 8 heads against a tile
+// of 16 tokens are a dense 16 x 16 product (heads padded to 16), so q.k and
+// P.V run on matrix cores:
+//
+//   S^T[16 tok][16 head] = K[16 tok][256] . Q^T[256][16 head]
+//       8 x v_mfma_f32_16x16x32_bf16; K enters as the A operand straight from
+//       its 16-byte row pieces (lane = token, 8 consecutive dims), q as B.
+//   O[16 head][256]     += P[16 head][16 tok] . V[16 tok][256]
+//       16 x v_mfma_f32_16x16x16_bf16, one per 16 output dims.  The S^T
+//       accumulator already holds P in the A-operand layout (lane = head,
+//       four consecutive tokens), so P never moves; V goes through LDS and
+//       comes back transposed by ds_read_b64_tr_b16 (lane = dim, four
+//       consecutive tokens), with an XOR swizzle on the 8-byte chunks that
+//       keeps the transposed reads free of bank conflicts.
+//
+// The online softmax (FP32, base 2, m per head) runs on the S^T accumulator:
+// each head's 16 scores sit in one column spread over the four 16-lane
+// groups.  W waves take 16-token tiles round-robin; their states are merged
+// through LDS in wave order at the end.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
+#include "pda_geometry.h"
 #include "pda_kernels.h"
 
 namespace pda {
+namespace {
 
-hipError_t launch_packed(const PackedParams&, uint32_t, hipStream_t) {
-    return hipErrorNotSupported;
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kD = 256;            // packed head dim
+constexpr int kG = 8;              // packed query heads per KV head
+constexpr int kTile = 16;          // tokens per tile
+constexpr int kWaves = 8;          // waves per workgroup
+constexpr int kVTileElems = kTile * kD;   // one wave's V tile in LDS (8 KiB)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2_t v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Values of the lower and upper 32-lane halves, and of the even and odd
+// 16-lane rows of this lane's pair (identical bits on both partners).
+__device__ __forceinline__ void halves(float x, float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void rowpair(float x, float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+// Max / sum over the four 16-lane groups (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float group_max(float x) {
+    float a, b;
+    rowpair(x, a, b);
+    x = fmaxf(a, b);
+    halves(x, a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float group_sum(float x) {
+    float a, b;
+    rowpair(x, a, b);
+    x = a + b;
+    halves(x, a, b);
+    return a + b;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Element offset of 8-byte chunk `chunk` (0..63) of token row `row` in a V
+// tile: chunks are XOR-swizzled by 4 * (row & 7) so that the four rows a
+// 16-lane group reads at once, in both 32-lane halves, hit distinct banks.
+__device__ __forceinline__ int vchunk(int row, int chunk) {
+    return row * kD + ((chunk ^ ((row & 7) << 2)) << 2);
+}
+
+__device__ __forceinline__ int clamp_len(int x, int cap) {
+    return x < 0 ? 0 : (x > cap ? cap : x);
+}
+
+// Rank -> sequence, longest first (ties by index); the same schedule rule as
+// the split-K fold.  Only the order of work depends on it.
+__device__ int packed_seq_of_rank(const int32_t* __restrict__ lens, int S, int r, int cap) {
+    if (S > 256) return r;
+    const int lane = (int)__lane_id();
+    int found = -1;
+    for (int base = 0; base < S; base += 64) {
+        const int i = base + lane;
+        const int Li = i < S ? clamp_len(lens[i], cap) : -1;
+        int cnt = 0;
+        for (int j = 0; j < S; ++j) {
+            const int Lj = clamp_len(lens[j], cap);
+            cnt += (Lj > Li) | ((Lj == Li) & (j < i));
+        }
+        if (i < S && cnt == r) found = i;
+    }
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(found >= 0);
+    const int src = mask ? __builtin_ctzll(mask) : 0;
+    return __builtin_amdgcn_readlane(found, src);
+}
+
+__global__ __launch_bounds__(64 * kWaves, 1) void packed_kernel(const PackedParams p) {
+    extern __shared__ __align__(16) uint16_t smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c = lane & 15;   // 16-lane group, lane in group
+    const int kvh = blockIdx.x;
+    const int cap = p.table_stride * p.bs;
+    const int seq = packed_seq_of_rank(p.lens, (int)gridDim.y, (int)blockIdx.y, cap);
+    const int L = clamp_len(p.lens[seq], cap);
+    const int64_t q_row = (int64_t)seq * p.nq + (int64_t)kvh * kG;   // first q slot
+
+    // q as the B operand: lane = head c (zeros for the 8 padding heads),
+    // 8 consecutive dims 32 * kb + 8 * g of k-step kb.
+    bf16x8_t qb[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (c < kG) w = *reinterpret_cast<const u32x4_t*>(p.q + (q_row + c) * kD + kb * 32 + g * 8);
+        qb[kb] = __builtin_bit_cast(bf16x8_t, w);
+    }
+
+    f32x4_t O[16];   // O[head 4g + r][dim 16 nb + c]
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, l = 0.f;   // of head c (same in all four groups)
+
+    uint16_t* vt = smem + wave * kVTileElems;
+    const int32_t* blocks = p.tables + (int64_t)seq * p.table_stride;
+    const uint16_t* kbase = p.k + (int64_t)kvh * p.kvh_s;
+    const uint16_t* vbase = p.v + (int64_t)kvh * p.kvh_s;
+    const int tiles = (L + kTile - 1) / kTile;
+
+    for (int t = wave; t < tiles; t += kWaves) {
+        const int tok0 = t * kTile;
+        const int b = tok0 / p.bs;
+        const int slot0 = tok0 - b * p.bs;
+        const int blk = blocks[b];
+        if ((uint32_t)blk >= p.num_blocks) continue;  // dropped: never dereferenced
+        const int nvalid = min(kTile, L - tok0);
+        const uint16_t* kblk = kbase + (int64_t)blk * p.blk_s + (int64_t)slot0 * p.tok_s;
+        const uint16_t* vblk = vbase + (int64_t)blk * p.blk_s + (int64_t)slot0 * p.tok_s;
+
+        // K as the A operand (lane = token c); a masked token re-reads the
+        // tile's first row, so canary memory never enters the arithmetic
+        const int tk = c < nvalid ? c : 0;
+        bf16x8_t ka[8];
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+            ka[kb] = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const u32x4_t*>(kblk + (int64_t)tk * p.tok_s +
+                                                            kb * 32 + g * 8));
+        // V rows in natural order: load i covers tokens 2i and 2i + 1
+        u32x4_t vr[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 2 * i + (lane >> 5);
+            const int tv = row < nvalid ? row : 0;
+            vr[i] = *reinterpret_cast<const u32x4_t*>(vblk + (int64_t)tv * p.tok_s + (lane & 31) * 8);
+        }
+
+        // S^T = K . Q^T ; acc[r] = score of token 4g + r for head c
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb], qb[kb], acc, 0, 0, 0);
+
+        float s[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] = 4 * g + r < nvalid ? acc[r] * p.c : kNegInf;
+        const float tmax = group_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+        const float mn = fmaxf(m, tmax);
+        const float ms = mn == kNegInf ? 0.f : mn;
+        const float alpha = fexp2(m - ms);
+        const bool grow = mn != m;
+        m = mn;
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pr[r] = c < kG ? fexp2(s[r] - ms) : 0.f;
+        l = l * alpha + group_sum((pr[0] + pr[1]) + (pr[2] + pr[3]));
+
+        // P as the A operand: lane = head c, tokens 4g .. 4g + 3 (in place)
+        const s16x4_t pa = __builtin_bit_cast(
+            s16x4_t, uint64_t(pack_bf16x2(pr[0], pr[1])) | (uint64_t(pack_bf16x2(pr[2], pr[3])) << 32));
+
+        // V tile -> LDS (swizzled rows), then rescale o while the writes land
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 2 * i + (lane >> 5);
+            *reinterpret_cast<u32x4_t*>(vt + vchunk(row, 2 * (lane & 31))) = vr[i];
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            // O rows are heads 4g + r; their factor lives in lane 4g + r
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float a = __int_as_float(
+                    __builtin_amdgcn_ds_bpermute((4 * g + r) * 4, __float_as_int(alpha)));
+#pragma unroll
+                for (int nb = 0; nb < 16; ++nb) O[nb][r] *= a;
+            }
+        }
+        wave_lds_sync();
+
+        // O += P . V, 16 output dims at a time; V^T read transposed from LDS:
+        // lane c of group g addresses row 4g + c/4, chunk 4 nb + c%4
+        const int trow = 4 * g + (c >> 2);
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) {
+            typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_p;
+            const uint16_t* src = vt + vchunk(trow, 4 * nb + (c & 3));
+            const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_p)(__attribute__((address_space(3))) uint16_t*)src);
+            O[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nb], 0, 0, 0);
+        }
+        wave_lds_sync();  // the next tile overwrites this wave's V tile
+    }
+
+    // Merge the waves in order.  LDS (reusing the V tiles): per wave and
+    // real head m and l, then o for one half of the dims at a time.
+    __syncthreads();
+    float* ml = reinterpret_cast<float*>(smem);                 // [W][8][2]
+    float* ow = ml + kWaves * kG * 2;                           // [W][8][128]
+    if (g == 0 && c < kG) {
+        ml[(wave * kG + c) * 2] = m;
+        ml[(wave * kG + c) * 2 + 1] = l;
+    }
+    __syncthreads();
+    // per head: max, weights, L (every thread computes the 8 heads' values
+    // it needs; cheap at 8 waves)
+    for (int half = 0; half < 2; ++half) {
+        // waves write the real heads' o (groups 0 and 1 hold heads 0..7)
+        if (g < 2) {
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    ow[(wave * kG + 4 * g + r) * 128 + nb * 16 + c] = O[half * 8 + nb][r];
+        }
+        __syncthreads();
+        for (int i = tid; i < kG * 64; i += 64 * kWaves) {
+            const int h = i / 64, d2 = (i % 64) * 2;     // two dims of this half
+            float M = kNegInf;
+            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[(w * kG + h) * 2]);
+            const float Ms = M == kNegInf ? 0.f : M;
+            float Lsum = 0.f, o0 = 0.f, o1 = 0.f;
+            for (int w = 0; w < kWaves; ++w) {
+                const float wt = fexp2(ml[(w * kG + h) * 2] - Ms);
+                Lsum += wt * ml[(w * kG + h) * 2 + 1];
+                o0 += wt * ow[(w * kG + h) * 128 + d2];
+                o1 += wt * ow[(w * kG + h) * 128 + d2 + 1];
+            }
+            const uint32_t v = Lsum > 0.f ? pack_bf16x2(o0 / Lsum, o1 / Lsum) : 0u;
+            *reinterpret_cast<uint32_t*>(p.out + (q_row + h) * kD + half * 128 + d2) = v;
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream) {
+    const size_t lds = sizeof(uint16_t) * (size_t)kWaves * kVTileElems;   // 64 KiB
+    hipLaunchKernelGGL(packed_kernel, dim3((uint32_t)p.nkv, num_seqs), dim3(64 * kWaves), lds,
+                       stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace pda

@@ -155,3 +155,44 @@ def test_batch_invariance_auto_and_pinned():
         for s in range(128):
             _, one, _ = dev.run(n, rows=[s])
             assert np.array_equal(host_bits(one)[0], full[s]), f"seq {s} differs alone (n={n})"
+
+
+def test_packed_mfma_workload():
+    """GQA-packed MFMA kernel (8 q heads x head_dim 256 per workgroup, one
+    split) on the packed workload, against the oracle and the unpacked path."""
+    say("[packed mfma]")
+    inp = W.make_paged("packed", canary=True)
+    assert P.pda_gqa_pack_shape_ok(32, 4, 256)
+    dev = PagedOnDevice(inp)
+    rc, out, _ = dev.run(1, packed=True)
+    assert rc == P.PDA_OK
+    ref, _, _ = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
+                               inp.scale)
+    got = host_bf16(out)
+    assert_out_close(got, ref, "packed")
+    _, out_u, _ = dev.run(1)
+    assert_out_close(host_bf16(out_u), ref, "unpacked")
+    # batch invariance of the packed launch
+    full = host_bits(out)
+    for s in (0, 13, 63):
+        _, one, _ = dev.run(1, packed=True, rows=[s])
+        assert np.array_equal(host_bits(one)[0], full[s]), f"packed seq {s} differs alone"
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_packed_mfma_edges(bs):
+    lens = (0, 1, 15, 16, 17, 100, 333)
+    say(f"[packed edges] bs={bs}")
+    base = W.Workload(name="pedge", seed=14, num_seqs=len(lens), num_q_heads=16, num_kv_heads=2,
+                      head_dim=256, block_size=bs, seq_lens=lens)
+    inp = W.make_paged(base, canary=True)
+    dev = PagedOnDevice(inp)
+    rc, out, _ = dev.run(1, packed=True)
+    assert rc == P.PDA_OK
+    ref, _, _ = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
+                               inp.scale)
+    assert_out_close(host_bf16(out), ref, "packed edges")
+    assert np.all(host_bits(out)[0] == 0)
+    # the packed gate: other shapes or a split launch are not applicable
+    rc, _, _ = dev.run(2, packed=True)
+    assert rc == P.PDA_NOT_APPLICABLE
