@@ -105,10 +105,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // order of length (ties by index), so the hardware dispatcher, which hands
 // out workgroups in id order, schedules the longest work first and the grid
 // drains with short work items (longest-processing-time-first).  Only the
-// schedule changes; each item's arithmetic is the same in any order.  Every
-// wave ranks the lengths itself (a few scalar loads and compares), which is
-// cheap up to kRankMax sequences; larger batches keep their given order.
-constexpr int kRankMax = 256;
+// schedule changes; each item's arithmetic is the same in any order.
+//
+// Every wave ranks the lengths itself: one wave-wide load of up to 64
+// lengths, then one compare per sequence against a value read from another
+// lane (v_readlane), so the cost is one memory round trip, not one per
+// sequence.  The sort key packs the length (saturated at 2^23 - 1, which
+// only coarsens the schedule of longer sequences) above the inverted index,
+// so keys are distinct and a larger key ranks first.  Batches of more than
+// kRankMax sequences keep their given order.
+constexpr int kRankMax = 64;
 
 __device__ __forceinline__ int clamp_len(int x, int cap) {
     return x < 0 ? 0 : (x > cap ? cap : x);
@@ -117,23 +123,23 @@ __device__ __forceinline__ int clamp_len(int x, int cap) {
 #ifndef PDA_FOLD_LPT
 #define PDA_FOLD_LPT 1
 #endif
-__device__ int seq_of_rank(const int32_t* __restrict__ lens, int S, int r, int cap) {
-    if (!PDA_FOLD_LPT || S > kRankMax) return r;
-    const int lane = (int)__lane_id();
-    int found = -1;
-    for (int base = 0; base < S; base += 64) {
-        const int i = base + lane;
-        const int Li = i < S ? clamp_len(lens[i], cap) : -1;
-        int cnt = 0;
-        for (int j = 0; j < S; ++j) {
-            const int Lj = clamp_len(lens[j], cap);
-            cnt += (Lj > Li) | ((Lj == Li) & (j < i));
-        }
-        if (i < S && cnt == r) found = i;
+// The sequence this workgroup works on and its length clamped to [0, cap].
+__device__ __forceinline__ void seq_of_rank(const int32_t* __restrict__ lens, int S, int r,
+                                            int cap, int& seq, int& len) {
+    if (!PDA_FOLD_LPT || S > kRankMax) {
+        seq = r;
+        len = clamp_len(lens[r], cap);
+        return;
     }
-    const uint64_t mask = __builtin_amdgcn_ballot_w64(found >= 0);
+    const int lane = (int)__lane_id();
+    const int Li = lane < S ? clamp_len(lens[lane], cap) : -1;
+    const int key = lane < S ? (min(Li, (1 << 23) - 1) << 8) | (255 - lane) : -1;
+    int cnt = 0;
+    for (int j = 0; j < S; ++j) cnt += __builtin_amdgcn_readlane(key, j) > key;
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(lane < S && cnt == r);
     const int src = mask ? __builtin_ctzll(mask) : 0;
-    return __builtin_amdgcn_readlane(found, src);
+    seq = src;
+    len = __builtin_amdgcn_readlane(Li, src);
 }
 
 // Cache policy of the K/V loads: non-temporal (each K/V byte is read once;
@@ -175,8 +181,9 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nw = blockDim.x >> 6;
     const int row = lane / LPT, sub = lane % LPT;
-    const int seq = seq_of_rank(p.lens, (int)gridDim.y, (int)blockIdx.y,
-                                MODE == kModeTiled ? p.table_stride : p.table_stride * p.bs);
+    int seq, slen;   // slen: tokens (one-shot) or tile blocks (tiled), clamped
+    seq_of_rank(p.lens, (int)gridDim.y, (int)blockIdx.y,
+                MODE == kModeTiled ? p.table_stride : p.table_stride * p.bs, seq, slen);
     const int per_seq = p.nkv * p.HG;
     const int kvhg = MODE == kModeTiled ? (int)blockIdx.x : (int)blockIdx.x % per_seq;
     const int split = MODE == kModeTiled ? 0 : (int)blockIdx.x / per_seq;
@@ -187,15 +194,12 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
     const int32_t* blocks = p.tables + (int64_t)seq * p.table_stride;
     int t_begin, t_end;
     if constexpr (MODE == kModeTiled) {
-        int cnt = p.lens[seq];
-        cnt = cnt < 0 ? 0 : (cnt > p.table_stride ? p.table_stride : cnt);
+        const int cnt = slen;
         if (cnt == 0) return;  // an empty tile leaves the state bit-identical
         t_begin = 0;
         t_end = (cnt - 1) * p.bs + p.lbvs;
     } else {
-        int L = p.lens[seq];
-        const int cap = p.table_stride * p.bs;
-        L = L < 0 ? 0 : (L > cap ? cap : L);
+        const int L = slen;
         const int chunk = (int)split_chunk((uint32_t)L, (uint32_t)p.nsplit, (uint32_t)p.bs);
         const int64_t b0 = (int64_t)split * chunk;
         t_begin = b0 < L ? (int)b0 : L;
@@ -218,16 +222,17 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
         }
     }
 
-    // q pieces of the group's heads (zeros for heads past gcount).
+    // q pieces of the group's heads (zeros for heads past gcount).  The
+    // loads are unconditional (a head past gcount re-reads the last one) so
+    // that they issue back to back with no branch between them.
     uint32_t q2[GC][4];
 #pragma unroll
     for (int h = 0; h < GC; ++h) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (h < gcount)
-            w = *reinterpret_cast<const u32x4*>(p.q + ((int64_t)seq * p.nq + h0 + h) * D +
-                                                sub * 8);
+        const int hq = h < gcount ? h : gcount - 1;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(
+            p.q + ((int64_t)seq * p.nq + h0 + hq) * D + sub * 8);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) q2[h][j] = w[j];
+        for (int j = 0; j < 4; ++j) q2[h][j] = h < gcount ? w[j] : 0u;
     }
 
     // Row state: o for every head (this lane's 8 dims); m and l for the
@@ -264,10 +269,25 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
     const uint16_t* kh = p.k + (int64_t)kvh * p.kvh_s;
     const uint16_t* vh = p.v + (int64_t)kvh * p.kvh_s;
 
+    // Block ids of the range in windows of 64: lane i holds the id of block
+    // b_lo + wbase + i, and the next window is requested one window ahead,
+    // so a group reads its block id from a register (v_readlane) instead of
+    // waiting on a table load before its K/V loads can start.
+    const int b_lo = g_first / gpb;
+    const int nbk = g_end > g_first ? (g_end - 1) / gpb - b_lo + 1 : 0;  // blocks in range
+    int wbase = 0;
+    int bw = lane < nbk ? blocks[b_lo + lane] : -1;
+    int bw_next = lane + 64 < nbk ? blocks[b_lo + 64 + lane] : -1;
+
     for (int g = g_first + wave; g < g_end; g += nw) {
         const int b = g / gpb;
         const int slot0 = (g - b * gpb) * TG;
-        const int blk = blocks[b];
+        while (b - b_lo - wbase >= 64) {   // wave-uniform; at most once per 64 blocks
+            wbase += 64;
+            bw = bw_next;
+            bw_next = lane + wbase + 64 < nbk ? blocks[b_lo + wbase + 64 + lane] : -1;
+        }
+        const int blk = __builtin_amdgcn_readlane(bw, b - b_lo - wbase);
         if ((uint32_t)blk >= p.num_blocks) continue;  // dropped: never dereferenced
         const int nvalid = min(TG, t_end - g * TG);
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh + (int64_t)blk * p.blk_s, rec);
