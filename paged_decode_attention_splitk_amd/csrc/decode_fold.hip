@@ -96,8 +96,16 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // Buffer descriptor over `bytes` bytes from `base` (raw, unswizzled; reads
 // past the range return 0).
+// The base and size are wave-uniform; readfirstlane makes that explicit so
+// the descriptor always lives in scalar registers (a descriptor the compiler
+// cannot prove uniform costs a loop over lanes around every load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes),
                                              0x00020000);
 }
 
@@ -476,10 +484,25 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
             ew[NC * GC + h] = wo;
             L = wo * l_old;
         }
-        for (int c = 0; c < NC; ++c) {
-            const float wt = fexp2(em[c * GC + h] - Ms);
-            ew[c * GC + h] = wt;
-            L += wt * el[c * GC + h];
+        // chunks of 8 contributors: all reads of a chunk are issued before
+        // its writes (the compiler cannot tell ew from em / el, so a write
+        // between reads would make every read wait for it)
+        for (int c0 = 0; c0 < NC; c0 += 8) {
+            float mv[8], lv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = c0 + j < NC ? c0 + j : NC - 1;
+                mv[j] = em[c * GC + h];
+                lv[j] = el[c * GC + h];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (c0 + j < NC) {
+                    const float wt = fexp2(mv[j] - Ms);
+                    ew[(c0 + j) * GC + h] = wt;
+                    L += wt * lv[j];
+                }
+            }
         }
         eL[h] = L;
         const float m_nat = M * kLn2;

@@ -31,11 +31,13 @@ constexpr uint32_t kBlockQuantum = 16;
 // Tokens of one split of a sequence of `seq_len` tokens: ceil(L / n) floored
 // at kMinKvPerSplit and rounded up to whole blocks, so every split starts on
 // a block boundary.  0 when n or block_size is 0.
+// Only 32-bit divisions (ceil written as quotient plus a remainder test),
+// so a kernel that calls it keeps no 64-bit division constants live.
 PDA_HD uint32_t split_chunk(uint32_t seq_len, uint32_t n, uint32_t block_size) {
     if (n == 0 || block_size == 0) return 0;
-    uint64_t per = ((uint64_t)seq_len + n - 1) / n;
+    uint32_t per = seq_len / n + (seq_len % n != 0u ? 1u : 0u);
     if (per < kMinKvPerSplit) per = kMinKvPerSplit;
-    uint64_t c = (per + block_size - 1) / block_size * block_size;
+    const uint64_t c = (uint64_t)((per - 1u) / block_size + 1u) * block_size;
     return c > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)c;
 }
 
