@@ -62,6 +62,8 @@ extern "C" {
 /* pda_paged_decode flags. */
 #define PDA_DECODE_UNPACKED 0u /* split-K kernel + merge (any shape)      */
 #define PDA_DECODE_PACKED 1u   /* GQA-packed MFMA kernel, or NOT_APPLICABLE */
+#define PDA_DECODE_DEFAULT 2u  /* packed iff pda_gqa_pack_enabled() and it
+                                  applies, else unpacked; never NOT_APPLICABLE */
 
 /* ------------------------------------------------------------------------
  * Constants.
@@ -123,6 +125,53 @@ uint64_t pda_gqa_pack_ctas(uint32_t num_kv_heads, uint32_t num_seqs);
  * seq_len is empty.  0 if num_splits or block_size is 0. */
 uint32_t pda_split_chunk(uint32_t seq_len, uint32_t num_splits, uint32_t block_size);
 
+/* ------------------------------------------------------------------------
+ * Policy resolution (attn_splitk page: parse, parse_gqa_pack,
+ * resolve_policy, policy_from_env, resolve_gqa_pack, gqa_pack_enabled,
+ * DECODE_GQA_PACK_DECLARED).  Host-only; no HIP calls.  Text is trimmed of
+ * ASCII whitespace and compared without regard to ASCII case.
+ * ------------------------------------------------------------------------ */
+
+/* A split-count policy: PDA_SPLITK_* and, for Pinned, the split count. */
+typedef struct {
+    int32_t policy;
+    uint32_t pin;
+} pda_splitk_policy;
+
+/* "legacy" -> Legacy; "auto" -> Auto; "0" / "off" / "false" / "no" -> Pinned
+ * 1 (split-K off); a decimal count (ASCII digits) -> Pinned, clamped to
+ * 1..pda_max_decode_splits() (too large a number saturates first).
+ * Returns 1 and fills *out when `s` parses, else 0 (also for NULL). */
+int pda_parse_splitk_policy(const char* s, pda_splitk_policy* out);
+
+/* "1" / "on" / "true" / "yes" -> 1; "0" / "off" / "false" / "no" -> 0.
+ * Returns 1 and fills *on when `s` parses, else 0 (also for NULL). */
+int pda_parse_gqa_pack(const char* s, int* on);
+
+/* The split-count declaration this library carries for MI355X: "auto". */
+const char* pda_splitk_declared(void);
+
+/* `declared`, overridden by `env_value` when that parses; a declaration
+ * that does not parse is Legacy.  env_value NULL means unset.  Pure. */
+void pda_resolve_policy(const char* declared, const char* env_value, pda_splitk_policy* out);
+
+/* pda_resolve_policy(pda_splitk_declared(),
+ * getenv("METRALE_ATTN_DECODE_SPLITK")); reads the environment each call. */
+void pda_policy_from_env(pda_splitk_policy* out);
+
+/* DECODE_GQA_PACK_DECLARED: the packed kernel is declared off (0). */
+int pda_decode_gqa_pack_declared(void);
+
+/* `declared` (0 / 1), overridden by `env_value` when that parses.  Pure. */
+int pda_resolve_gqa_pack(int declared, const char* env_value);
+
+/* Whether the packed kernel is armed in this process:
+ * pda_resolve_gqa_pack(pda_decode_gqa_pack_declared(),
+ * getenv("METRALE_ATTN_DECODE_GQA_PACK")), resolved on the first call and
+ * fixed for the life of the process (so captured launches stay consistent
+ * with later ones).  Thread-safe. */
+int pda_gqa_pack_enabled(void);
+
 /* Compute units of HIP device `device` (the cu_count the policies take). */
 int pda_device_cu_count(int device, uint32_t* cu_count);
 
@@ -148,7 +197,10 @@ int pda_device_cu_count(int device, uint32_t* cu_count);
  *   flags        PDA_DECODE_UNPACKED, or PDA_DECODE_PACKED to run the
  *                GQA-packed MFMA kernel, which serves only
  *                pda_gqa_pack_shape_ok shapes at num_splits == 1 (else
- *                PDA_NOT_APPLICABLE, nothing launched).
+ *                PDA_NOT_APPLICABLE, nothing launched), or
+ *                PDA_DECODE_DEFAULT: the packed kernel when
+ *                pda_gqa_pack_enabled() and it applies, the unpacked path
+ *                otherwise.
  *
  * Requirements: num_kv_heads > 0, num_q_heads % num_kv_heads == 0,
  * head_dim in {64, 128, 256}, block_size a positive multiple of 16, q /

@@ -14,6 +14,9 @@ Contents
                       partials, tiled running state).
 ``oracle.geometry``   the launch-geometry formulas of the attn_splitk module
                       page, written out in Python integers.
+``oracle.policy``     that page's policy grammar and resolution rules
+                      (parse, parse_gqa_pack, resolve_policy,
+                      resolve_gqa_pack).
 
 Pins (what each function is checked against, in ``tests/test_oracle_*.py``):
 brute-force pure-Python loops on tiny inputs, torch's FP64

@@ -11,7 +11,7 @@ the library's HIP kernels; nothing here computes attention.
 that take torch tensors and derive the sizes from their shapes.
 
 Importing this module raises ``ImportError`` if ``libpda.so`` has not been
-built (``python -m paged_decode_attention_splitk_amd._build``); there is no
+built (``python paged_decode_attention_splitk_amd/_build.py``); there is no
 fallback implementation.
 """
 from __future__ import annotations
@@ -32,7 +32,7 @@ LIB_PATH = os.path.join(_HERE, "libpda.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m paged_decode_attention_splitk_amd._build` "
+        f"{LIB_PATH} is missing: build it with `python paged_decode_attention_splitk_amd/_build.py` "
         "(hipcc, gfx950). There is no CPU fallback.")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -49,9 +49,17 @@ PDA_SPLITK_PINNED = 2
 
 PDA_DECODE_UNPACKED = 0
 PDA_DECODE_PACKED = 1
+PDA_DECODE_DEFAULT = 2
 
 _u32, _u64, _i32, _i64 = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int64
 _vp, _f32, _int = ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+
+
+class pda_splitk_policy(ctypes.Structure):
+    _fields_ = [("policy", _i32), ("pin", _u32)]
+
+    def astuple(self):
+        return (self.policy, self.pin)
 
 
 class pda_tiled_dims(ctypes.Structure):
@@ -76,6 +84,15 @@ _SIGS = {
     "pda_gqa_pack_ctas": (_u64, [_u32, _u32]),
     "pda_split_chunk": (_u32, [_u32, _u32, _u32]),
     "pda_device_cu_count": (_int, [_int, ctypes.POINTER(_u32)]),
+    "pda_parse_splitk_policy": (_int, [ctypes.c_char_p, ctypes.POINTER(pda_splitk_policy)]),
+    "pda_parse_gqa_pack": (_int, [ctypes.c_char_p, ctypes.POINTER(_int)]),
+    "pda_splitk_declared": (ctypes.c_char_p, []),
+    "pda_resolve_policy": (None, [ctypes.c_char_p, ctypes.c_char_p,
+                                  ctypes.POINTER(pda_splitk_policy)]),
+    "pda_policy_from_env": (None, [ctypes.POINTER(pda_splitk_policy)]),
+    "pda_decode_gqa_pack_declared": (_int, []),
+    "pda_resolve_gqa_pack": (_int, [_int, ctypes.c_char_p]),
+    "pda_gqa_pack_enabled": (_int, []),
     "pda_paged_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _u64, _u32, _u32, _u32,
                                 _u32, _u32, _u32, _u32, _f32, _u32, _u32, _vp]),
     "pda_splitk_merge": (_int, [_vp, _u64, _vp, _u32, _u32, _u32, _u32, _vp]),
@@ -168,6 +185,46 @@ def pda_device_cu_count(device: int = 0) -> int:
     n = _u32(0)
     _check(_lib.pda_device_cu_count(device, ctypes.byref(n)))
     return n.value
+
+
+# ---------------------------------------------------------------- policy
+def _cstr(x):
+    if x is None:
+        return None
+    return x.encode() if isinstance(x, str) else bytes(x)
+
+
+def pda_parse_splitk_policy(s):
+    """(policy, pin) for a parseable string, else None."""
+    p = pda_splitk_policy()
+    return p.astuple() if _lib.pda_parse_splitk_policy(_cstr(s), ctypes.byref(p)) else None
+
+
+def pda_parse_gqa_pack(s):
+    """True / False for a parseable string, else None."""
+    on = _int(0)
+    return bool(on.value) if _lib.pda_parse_gqa_pack(_cstr(s), ctypes.byref(on)) else None
+
+
+def pda_splitk_declared() -> str: return _lib.pda_splitk_declared().decode()
+
+
+def pda_resolve_policy(declared, env_value):
+    p = pda_splitk_policy()
+    _lib.pda_resolve_policy(_cstr(declared), _cstr(env_value), ctypes.byref(p))
+    return p.astuple()
+
+
+def pda_policy_from_env():
+    p = pda_splitk_policy()
+    _lib.pda_policy_from_env(ctypes.byref(p))
+    return p.astuple()
+
+
+def pda_decode_gqa_pack_declared() -> bool: return bool(_lib.pda_decode_gqa_pack_declared())
+def pda_resolve_gqa_pack(declared, env_value) -> bool:
+    return bool(_lib.pda_resolve_gqa_pack(int(bool(declared)), _cstr(env_value)))
+def pda_gqa_pack_enabled() -> bool: return bool(_lib.pda_gqa_pack_enabled())
 
 
 def pda_last_error() -> str:

@@ -1,6 +1,7 @@
 """Build ``libpda.so`` (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-Usage: ``python -m paged_decode_attention_splitk_amd._build`` or
+Usage: ``python paged_decode_attention_splitk_amd/_build.py`` (run as a script, so a stale
+libpda.so is never loaded first) or
 ``__graft_entry__.build()``.  Objects go to ``_build/`` at the repository
 root; the library lands next to this file.
 """

@@ -221,14 +221,19 @@ int pda_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                         block_size, max_blocks_per_seq, num_blocks};
     int rc = check_decode(s, q, k_cache, v_cache, block_tables, seq_lens, out, true);
     if (rc != PDA_OK) return rc;
-    if (flags & ~PDA_DECODE_PACKED) return fail(PDA_EINVAL, "unknown flags 0x%x", flags);
+    if (flags > PDA_DECODE_DEFAULT) return fail(PDA_EINVAL, "unknown flags 0x%x", flags);
     if (num_splits < 1 || num_splits > pda::kMaxDecodeSplits)
         return fail(PDA_EINVAL, "num_splits %u outside 1..%u", num_splits, pda::kMaxDecodeSplits);
     if (!std::isfinite(scale)) return fail(PDA_EINVAL, "scale is not finite");
     hipStream_t st = (hipStream_t)stream;
 
-    if (flags & PDA_DECODE_PACKED) {
-        if (!pda_gqa_pack_shape_ok(num_q_heads, num_kv_heads, head_dim) || num_splits != 1) {
+    const bool pack_applies =
+        pda_gqa_pack_shape_ok(num_q_heads, num_kv_heads, head_dim) && num_splits == 1;
+    if (flags == PDA_DECODE_DEFAULT) flags = pack_applies && pda_gqa_pack_enabled()
+                                                 ? PDA_DECODE_PACKED
+                                                 : PDA_DECODE_UNPACKED;
+    if (flags == PDA_DECODE_PACKED) {
+        if (!pack_applies) {
             g_last_error = "packed kernel not applicable: needs num_q_heads == 8 * num_kv_heads, "
                            "head_dim 256 and num_splits 1";
             return PDA_NOT_APPLICABLE;

@@ -15,5 +15,9 @@ def pytest_sessionstart(session):
     # build the HIP library in-tree when it is missing (never rebuilds)
     lib = os.path.join(ROOT, "paged_decode_attention_splitk_amd", "libpda.so")
     if not os.path.exists(lib):
-        from paged_decode_attention_splitk_amd import _build
-        _build.build(verbose=True)
+        import importlib.util
+        path = os.path.join(ROOT, "paged_decode_attention_splitk_amd", "_build.py")
+        spec = importlib.util.spec_from_file_location("pda_build", path)
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)   # by path: never loads a stale library first
+        mod.build(verbose=True)

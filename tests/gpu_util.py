@@ -79,9 +79,10 @@ class PagedOnDevice:
         self.bt = dev_i32(inp.block_tables)
         self.lens = dev_i32(inp.seq_lens)
 
-    def run(self, num_splits, packed=False, rows=None, out=None, ws=None):
+    def run(self, num_splits, packed=False, rows=None, out=None, ws=None, flags=None):
         """Run pda_paged_decode; ``rows`` restricts to a subset of sequences
-        (their q rows / table rows / lengths, against the same pool)."""
+        (their q rows / table rows / lengths, against the same pool).
+        ``flags`` (a PDA_DECODE_* value) overrides ``packed``."""
         inp = self.inp
         q, bt, lens = self.q, self.bt, self.lens
         if rows is not None:
@@ -97,7 +98,8 @@ class PagedOnDevice:
         rc = P.pda_paged_decode(q, self.k, self.v, bt, lens, out, ws, wsf, S, nq,
                                 inp.num_kv_heads, D, inp.block_size, bt.shape[1],
                                 inp.num_blocks, inp.scale, num_splits,
-                                P.PDA_DECODE_PACKED if packed else P.PDA_DECODE_UNPACKED)
+                                flags if flags is not None else
+                                (P.PDA_DECODE_PACKED if packed else P.PDA_DECODE_UNPACKED))
         torch.cuda.synchronize()
         return rc, out, ws
 

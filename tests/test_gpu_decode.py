@@ -196,3 +196,89 @@ def test_packed_mfma_edges(bs):
     # the packed gate: other shapes or a split launch are not applicable
     rc, _, _ = dev.run(2, packed=True)
     assert rc == P.PDA_NOT_APPLICABLE
+
+
+def test_legacy_negative_control():
+    """Under Legacy the split count follows the batch once it passes
+    max_decode_seqs, so a sequence's output bytes change with what it is
+    batched with; under Auto they do not (attn_splitk page: the module
+    comment and its invariants).  Both stay within tolerance of the oracle."""
+    base = W.Workload(name="legacy", seed=15, num_seqs=16, num_q_heads=8, num_kv_heads=2,
+                      head_dim=128, block_size=16, len_range=(300, 1200))
+    inp = W.make_paged(base, canary=True)
+    dev = PagedOnDevice(inp)
+    ref, _, _ = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
+                               inp.scale)
+    rows = [0, 1, 2, 3]
+    mds = 4   # max_decode_seqs
+    n_small = P.pda_num_splits(P.PDA_SPLITK_LEGACY, 0, CU, 8, len(rows), mds)
+    n_big = P.pda_num_splits(P.PDA_SPLITK_LEGACY, 0, CU, 8, 16, mds)
+    assert (n_small, n_big) == (8, 2)        # 256 // (8 * 4), 256 // (8 * 16)
+    say(f"[legacy control] splits {n_small} / {n_big}")
+    _, small, _ = dev.run(n_small, rows=rows)
+    _, big, _ = dev.run(n_big)
+    assert_out_close(host_bf16(small), ref[rows], "legacy, 4 rows")
+    assert_out_close(host_bf16(big), ref, "legacy, 16 rows")
+    assert not np.array_equal(host_bits(small), host_bits(big)[rows])
+    n_a4 = P.pda_num_splits(P.PDA_SPLITK_AUTO, 0, CU, 8, len(rows), mds)
+    n_a16 = P.pda_num_splits(P.PDA_SPLITK_AUTO, 0, CU, 8, 16, mds)
+    assert n_a4 == n_a16
+    _, a_small, _ = dev.run(n_a4, rows=rows)
+    _, a_big, _ = dev.run(n_a16)
+    assert np.array_equal(host_bits(a_small), host_bits(a_big)[rows])
+
+
+def _pack_shape_inputs():
+    base = W.Workload(name="pdefault", seed=16, num_seqs=5, num_q_heads=16, num_kv_heads=2,
+                      head_dim=256, block_size=16, seq_lens=(7, 100, 257, 16, 1000))
+    return W.make_paged(base, canary=True)
+
+
+def test_default_flag_follows_gqa_pack_switch():
+    """PDA_DECODE_DEFAULT runs the packed kernel exactly when
+    pda_gqa_pack_enabled() (resolved once per process) and the launch is one
+    it serves; otherwise the unpacked path, and never NOT_APPLICABLE."""
+    inp = _pack_shape_inputs()
+    dev = PagedOnDevice(inp)
+    rc, d1, _ = dev.run(1, flags=P.PDA_DECODE_DEFAULT)
+    assert rc == P.PDA_OK
+    _, pk, _ = dev.run(1, packed=True)
+    _, up, _ = dev.run(1)
+    want = pk if P.pda_gqa_pack_enabled() else up
+    assert np.array_equal(host_bits(d1), host_bits(want))
+    # a split launch never takes the packed kernel
+    rc, d4, _ = dev.run(4, flags=P.PDA_DECODE_DEFAULT)
+    assert rc == P.PDA_OK
+    _, u4, _ = dev.run(4)
+    assert np.array_equal(host_bits(d4), host_bits(u4))
+
+
+_DEFAULT_CHILD = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np, torch
+import paged_decode_attention_splitk_amd as P
+from tests.gpu_util import PagedOnDevice, host_bits
+from tests.test_gpu_decode import _pack_shape_inputs
+assert P.pda_gqa_pack_enabled()
+dev = PagedOnDevice(_pack_shape_inputs())
+_, d, _ = dev.run(1, flags=P.PDA_DECODE_DEFAULT)
+_, pk, _ = dev.run(1, packed=True)
+_, up, _ = dev.run(1)
+assert np.array_equal(host_bits(d), host_bits(pk))
+assert not np.array_equal(host_bits(pk), host_bits(up))
+print("default->packed ok", flush=True)
+"""
+
+
+def test_default_flag_with_pack_switched_on_in_env():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, METRALE_ATTN_DECODE_GQA_PACK="on")
+    say("[default flag, pack on] child process")
+    r = subprocess.run([sys.executable, "-c", _DEFAULT_CHILD, root], env=env, cwd=root,
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert "default->packed ok" in r.stdout
