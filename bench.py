@@ -128,7 +128,7 @@ def main():
     if args.packed:
         if not P.pda_gqa_pack_shape_ok(nq, nkv, D):
             sys.exit(f"--packed needs 8 q heads per kv head at head_dim 256 (got {nq}/{nkv}/{D})")
-        n = 1
+        n = args.splits or 1   # the packed kernels' own (non-split) launch unless pinned
     ab = alg_bytes(inp, n)
     copies = args.copies or max(1, math.ceil(1.0e9 / ab["kv"]))
 
@@ -156,7 +156,7 @@ def main():
             assert rc == P.PDA_OK
         else:
             P.pda_splitk_partials(q, ks[i % copies], vs[i % copies], bt, lens, ws, wsf, S, nq,
-                                  nkv, D, bs, mb, inp.num_blocks, inp.scale, n, sp)
+                                  nkv, D, bs, mb, inp.num_blocks, inp.scale, n, flags, sp)
 
     def merge():
         if n > 1:
@@ -235,7 +235,8 @@ def main():
         "kernels_us": {"splitk_fold": round(fold_avg * 1e3, 2),
                        "splitk_merge": round(merge_avg * 1e3, 2)},
         "roofline": {
-            "kernel": ("GQA-packed MFMA decode (packed_kernel)" if args.packed else
+            "kernel": (f"GQA-packed MFMA decode (packed_kernel<{'true' if n > 1 else 'false'}>)"
+                       if args.packed else
                        f"split-K fold (fold_kernel<{0 if n > 1 else 1},{D},{min(nq // nkv, 8)}>)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),

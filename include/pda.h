@@ -194,13 +194,16 @@ int pda_device_cu_count(int device, uint32_t* cu_count);
  *                A sequence's output bytes depend on its own data, scale,
  *                num_splits and the shape only, never on the other rows of
  *                the batch.
- *   flags        PDA_DECODE_UNPACKED, or PDA_DECODE_PACKED to run the
+ *   flags        PDA_DECODE_UNPACKED; PDA_DECODE_PACKED to run the
  *                GQA-packed MFMA kernel, which serves only
- *                pda_gqa_pack_shape_ok shapes at num_splits == 1 (else
- *                PDA_NOT_APPLICABLE, nothing launched), or
+ *                pda_gqa_pack_shape_ok shapes (else PDA_NOT_APPLICABLE,
+ *                nothing launched), with num_splits == 1 (bf16 out
+ *                directly) or, as this library's extension of the pages'
+ *                non-split packed kernels, num_splits > 1 (the same
+ *                workspace partials and merge as the unpacked path); or
  *                PDA_DECODE_DEFAULT: the packed kernel when
- *                pda_gqa_pack_enabled() and it applies, the unpacked path
- *                otherwise.
+ *                pda_gqa_pack_enabled(), the shape qualifies and
+ *                num_splits == 1, the unpacked path otherwise.
  *
  * Requirements: num_kv_heads > 0, num_q_heads % num_kv_heads == 0,
  * head_dim in {64, 128, 256}, block_size a positive multiple of 16, q /
@@ -224,13 +227,15 @@ int pda_splitk_merge(const float* workspace, uint64_t workspace_floats, void* ou
                      uint32_t num_splits, void* stream);
 
 /* pda_paged_decode without the merge: leaves the partials in the workspace
- * (num_splits >= 2). */
+ * (num_splits >= 2).  flags: PDA_DECODE_UNPACKED or PDA_DECODE_DEFAULT (the
+ * split-K fold kernel), or PDA_DECODE_PACKED (the packed MFMA kernel's
+ * split-K form; PDA_NOT_APPLICABLE unless pda_gqa_pack_shape_ok). */
 int pda_splitk_partials(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_tables, const int32_t* seq_lens,
                         float* workspace, uint64_t workspace_floats, uint32_t num_seqs,
                         uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
                         uint32_t block_size, uint32_t max_blocks_per_seq, uint32_t num_blocks,
-                        float scale, uint32_t num_splits, void* stream);
+                        float scale, uint32_t num_splits, uint32_t flags, void* stream);
 
 /* ------------------------------------------------------------------------
  * Tiled state API (tiled_attention.rs page: TiledAttention).

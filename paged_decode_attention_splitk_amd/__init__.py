@@ -97,7 +97,7 @@ _SIGS = {
                                 _u32, _u32, _u32, _u32, _f32, _u32, _u32, _vp]),
     "pda_splitk_merge": (_int, [_vp, _u64, _vp, _u32, _u32, _u32, _u32, _vp]),
     "pda_splitk_partials": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _u64, _u32, _u32, _u32, _u32,
-                                   _u32, _u32, _u32, _f32, _u32, _vp]),
+                                   _u32, _u32, _u32, _f32, _u32, _u32, _vp]),
     "pda_tiled_validate": (_int, [ctypes.POINTER(pda_tiled_dims)]),
     "pda_tiled_create": (_int, [ctypes.POINTER(pda_tiled_dims), ctypes.POINTER(_vp)]),
     "pda_tiled_destroy": (None, [_vp]),
@@ -251,11 +251,11 @@ def pda_splitk_merge(workspace, workspace_floats, out, num_seqs, num_q_heads, he
 def pda_splitk_partials(q, k_cache, v_cache, block_tables, seq_lens, workspace,
                         workspace_floats, num_seqs, num_q_heads, num_kv_heads, head_dim,
                         block_size, max_blocks_per_seq, num_blocks, scale, num_splits,
-                        stream=None) -> int:
+                        flags=PDA_DECODE_UNPACKED, stream=None) -> int:
     return _check(_lib.pda_splitk_partials(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         _ptr(workspace), workspace_floats, num_seqs, num_q_heads, num_kv_heads, head_dim,
-        block_size, max_blocks_per_seq, num_blocks, scale, num_splits, _stream(stream)))
+        block_size, max_blocks_per_seq, num_blocks, scale, num_splits, flags, _stream(stream)))
 
 
 # ---------------------------------------------------------------- tiled

@@ -132,15 +132,44 @@ pda::FoldParams fold_params(const DecodeShape& s, const void* q, const void* k, 
     return p;
 }
 
+pda::PackedParams packed_params(const DecodeShape& s, const void* q, const void* k,
+                                const void* v, const int32_t* bt, const int32_t* lens,
+                                float scale, uint32_t nsplit) {
+    pda::PackedParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.tables = bt;
+    p.lens = lens;
+    p.blk_s = (int64_t)s.bs * s.nkv * s.D;
+    p.tok_s = (int64_t)s.nkv * s.D;
+    p.kvh_s = s.D;
+    p.num_blocks = s.num_blocks;
+    p.nq = (int)s.nq;
+    p.nkv = (int)s.nkv;
+    p.bs = (int)s.bs;
+    p.table_stride = (int)s.max_blocks;
+    p.nsplit = (int)nsplit;
+    p.c = scale * kLog2e;
+    return p;
+}
+
 int run_partials(const DecodeShape& s, const void* q, const void* k, const void* v,
                  const int32_t* bt, const int32_t* lens, float* ws, uint64_t ws_floats,
-                 float scale, uint32_t nsplit, hipStream_t stream) {
+                 float scale, uint32_t nsplit, bool packed, hipStream_t stream) {
     if (!ws) return fail(PDA_EINVAL, "workspace is NULL with num_splits > 1");
     if (!aligned(ws, 8)) return fail(PDA_EINVAL, "workspace must be 8-byte aligned");
     const uint64_t need = pda_workspace_slots(s.num_seqs, s.nq, nsplit, s.D);
     if (ws_floats < need)
         return fail(PDA_EINVAL, "workspace holds %llu floats, needs %llu",
                     (unsigned long long)ws_floats, (unsigned long long)need);
+    if (packed) {
+        pda::PackedParams p = packed_params(s, q, k, v, bt, lens, scale, nsplit);
+        p.ws = ws;
+        hipError_t e = pda::launch_packed(p, s.num_seqs, stream);
+        if (e != hipSuccess) return hip_fail(e, "packed split-K partial launch");
+        return PDA_OK;
+    }
     int hg = 0;
     const int gc = head_groups(s.nq / s.nkv, &hg);
     pda::FoldParams p = fold_params(s, q, k, v, bt, lens, hg, scale, nsplit);
@@ -173,18 +202,25 @@ int pda_splitk_partials(const void* q, const void* k_cache, const void* v_cache,
                         uint64_t workspace_floats, uint32_t num_seqs, uint32_t num_q_heads,
                         uint32_t num_kv_heads, uint32_t head_dim, uint32_t block_size,
                         uint32_t max_blocks_per_seq, uint32_t num_blocks, float scale,
-                        uint32_t num_splits, void* stream) {
+                        uint32_t num_splits, uint32_t flags, void* stream) {
     const DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim,
                         block_size, max_blocks_per_seq, num_blocks};
     int rc = check_decode(s, q, k_cache, v_cache, block_tables, seq_lens, nullptr, false);
     if (rc != PDA_OK) return rc;
+    if (flags > PDA_DECODE_DEFAULT) return fail(PDA_EINVAL, "unknown flags 0x%x", flags);
     if (num_splits < 2 || num_splits > pda::kMaxDecodeSplits)
         return fail(PDA_EINVAL, "num_splits %u outside 2..%u for a partials launch", num_splits,
                     pda::kMaxDecodeSplits);
     if (!std::isfinite(scale)) return fail(PDA_EINVAL, "scale is not finite");
+    const bool packed = flags == PDA_DECODE_PACKED;
+    if (packed && !pda_gqa_pack_shape_ok(num_q_heads, num_kv_heads, head_dim)) {
+        g_last_error = "packed kernel not applicable: needs num_q_heads == 8 * num_kv_heads "
+                       "and head_dim 256";
+        return PDA_NOT_APPLICABLE;
+    }
     if (num_seqs == 0) return ok();
     rc = run_partials(s, q, k_cache, v_cache, block_tables, seq_lens, workspace, workspace_floats,
-                      scale, num_splits, (hipStream_t)stream);
+                      scale, num_splits, packed, (hipStream_t)stream);
     return rc == PDA_OK ? ok() : rc;
 }
 
@@ -227,40 +263,27 @@ int pda_paged_decode(const void* q, const void* k_cache, const void* v_cache,
     if (!std::isfinite(scale)) return fail(PDA_EINVAL, "scale is not finite");
     hipStream_t st = (hipStream_t)stream;
 
-    const bool pack_applies =
-        pda_gqa_pack_shape_ok(num_q_heads, num_kv_heads, head_dim) && num_splits == 1;
-    if (flags == PDA_DECODE_DEFAULT) flags = pack_applies && pda_gqa_pack_enabled()
-                                                 ? PDA_DECODE_PACKED
-                                                 : PDA_DECODE_UNPACKED;
-    if (flags == PDA_DECODE_PACKED) {
-        if (!pack_applies) {
-            g_last_error = "packed kernel not applicable: needs num_q_heads == 8 * num_kv_heads, "
-                           "head_dim 256 and num_splits 1";
-            return PDA_NOT_APPLICABLE;
-        }
-        if (num_seqs == 0) return ok();
-        pda::PackedParams p{};
-        p.q = static_cast<const uint16_t*>(q);
-        p.k = static_cast<const uint16_t*>(k_cache);
-        p.v = static_cast<const uint16_t*>(v_cache);
-        p.tables = block_tables;
-        p.lens = seq_lens;
+    const bool shape_packs = pda_gqa_pack_shape_ok(num_q_heads, num_kv_heads, head_dim);
+    // the default arms the packed kernel on non-split launches only, as the
+    // pages do; an explicit request also takes it with split-K
+    if (flags == PDA_DECODE_DEFAULT)
+        flags = shape_packs && num_splits == 1 && pda_gqa_pack_enabled() ? PDA_DECODE_PACKED
+                                                                          : PDA_DECODE_UNPACKED;
+    const bool packed = flags == PDA_DECODE_PACKED;
+    if (packed && !shape_packs) {
+        g_last_error = "packed kernel not applicable: needs num_q_heads == 8 * num_kv_heads "
+                       "and head_dim 256";
+        return PDA_NOT_APPLICABLE;
+    }
+    if (num_seqs == 0) return ok();
+    if (packed && num_splits == 1) {
+        pda::PackedParams p = packed_params(s, q, k_cache, v_cache, block_tables, seq_lens,
+                                            scale, 1);
         p.out = static_cast<uint16_t*>(out);
-        p.blk_s = (int64_t)block_size * num_kv_heads * head_dim;
-        p.tok_s = (int64_t)num_kv_heads * head_dim;
-        p.kvh_s = head_dim;
-        p.num_blocks = num_blocks;
-        p.nq = (int)num_q_heads;
-        p.nkv = (int)num_kv_heads;
-        p.bs = (int)block_size;
-        p.table_stride = (int)max_blocks_per_seq;
-        p.c = scale * kLog2e;
         hipError_t e = pda::launch_packed(p, num_seqs, st);
         if (e != hipSuccess) return hip_fail(e, "packed decode launch");
         return ok();
     }
-
-    if (num_seqs == 0) return ok();
     if (num_splits == 1) {
         int hg = 0;
         const int gc = head_groups(num_q_heads / num_kv_heads, &hg);
@@ -274,7 +297,7 @@ int pda_paged_decode(const void* q, const void* k_cache, const void* v_cache,
         return ok();
     }
     rc = run_partials(s, q, k_cache, v_cache, block_tables, seq_lens, workspace, workspace_floats,
-                      scale, num_splits, st);
+                      scale, num_splits, packed, st);
     if (rc != PDA_OK) return rc;
     hipError_t e = pda::launch_merge(workspace, static_cast<uint16_t*>(out), num_seqs,
                                      (int)num_q_heads, (int)head_dim, (int)num_splits, st);

@@ -20,6 +20,14 @@
 // each head's 16 scores sit in one column spread over the four 16-lane
 // groups.  W waves take 16-token tiles round-robin; their states are merged
 // through LDS in wave order at the end.
+//
+// The split-K form (SPLIT = true) takes one split of the sequence per
+// workgroup, with the split partition of the unpacked kernels, and leaves
+// each head's FP32 (o unnormalised, m natural-log, l) in the split-K
+// workspace slot that the merge kernel reads.  The pages arm the packed
+// kernels only on non-split launches; the split-K form is this library's
+// extension for long, uneven batches, where one workgroup per sequence and
+// KV head leaves the device waiting on the longest sequence.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,47 +103,74 @@ __device__ __forceinline__ int clamp_len(int x, int cap) {
     return x < 0 ? 0 : (x > cap ? cap : x);
 }
 
-// Rank -> sequence, longest first (ties by index); the same schedule rule as
-// the split-K fold.  Only the order of work depends on it.
-__device__ int packed_seq_of_rank(const int32_t* __restrict__ lens, int S, int r, int cap) {
-    if (S > 256) return r;
-    const int lane = (int)__lane_id();
-    int found = -1;
-    for (int base = 0; base < S; base += 64) {
-        const int i = base + lane;
-        const int Li = i < S ? clamp_len(lens[i], cap) : -1;
-        int cnt = 0;
-        for (int j = 0; j < S; ++j) {
-            const int Lj = clamp_len(lens[j], cap);
-            cnt += (Lj > Li) | ((Lj == Li) & (j < i));
-        }
-        if (i < S && cnt == r) found = i;
+// Rank -> sequence, longest first (ties by index), and its clamped length;
+// the same schedule rule as the split-K fold: one wave-wide load of the
+// lengths, one compare per sequence against a value read from another lane.
+// Batches of more than 64 sequences keep their order.  Only the order of
+// work depends on it.
+__device__ __forceinline__ void packed_seq_of_rank(const int32_t* __restrict__ lens, int S,
+                                                   int r, int cap, int& seq, int& len) {
+    if (S > 64) {
+        seq = r;
+        len = clamp_len(lens[r], cap);
+        return;
     }
-    const uint64_t mask = __builtin_amdgcn_ballot_w64(found >= 0);
+    const int lane = (int)__lane_id();
+    const int Li = lane < S ? clamp_len(lens[lane], cap) : -1;
+    const int key = lane < S ? (min(Li, (1 << 23) - 1) << 8) | (255 - lane) : -1;
+    int cnt = 0;
+    for (int j = 0; j < S; ++j) cnt += __builtin_amdgcn_readlane(key, j) > key;
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(lane < S && cnt == r);
     const int src = mask ? __builtin_ctzll(mask) : 0;
-    return __builtin_amdgcn_readlane(found, src);
+    seq = src;
+    len = __builtin_amdgcn_readlane(Li, src);
 }
 
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <bool SPLIT>
 __global__ __launch_bounds__(64 * kWaves, 1) void packed_kernel(const PackedParams p) {
     extern __shared__ __align__(16) uint16_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;   // 16-lane group, lane in group
-    const int kvh = blockIdx.x;
+    const int kvh = SPLIT ? (int)blockIdx.x % p.nkv : (int)blockIdx.x;
+    const int sp = SPLIT ? (int)blockIdx.x / p.nkv : 0;
     const int cap = p.table_stride * p.bs;
-    const int seq = packed_seq_of_rank(p.lens, (int)gridDim.y, (int)blockIdx.y, cap);
-    const int L = clamp_len(p.lens[seq], cap);
+    int seq, L;
+    packed_seq_of_rank(p.lens, (int)gridDim.y, (int)blockIdx.y, cap, seq, L);
     const int64_t q_row = (int64_t)seq * p.nq + (int64_t)kvh * kG;   // first q slot
 
+    // this workgroup's tokens: the whole sequence, or split sp of it
+    int t_begin = 0, t_end = L;
+    if constexpr (SPLIT) {
+        const int chunk = (int)split_chunk((uint32_t)L, (uint32_t)p.nsplit, (uint32_t)p.bs);
+        const int64_t b0 = (int64_t)sp * chunk;
+        t_begin = b0 < L ? (int)b0 : L;
+        t_end = (int64_t)t_begin + chunk < L ? t_begin + chunk : L;
+        if (t_begin >= t_end) {
+            // an empty split: m = -inf, l = 0 (its o is never read)
+            if (tid < kG) {
+                float* slot = p.ws + ((q_row + tid) * p.nsplit + sp) * (int64_t)(kD + 2);
+                slot[kD] = kNegInf;
+                slot[kD + 1] = 0.f;
+            }
+            return;
+        }
+    }
+
     // q as the B operand: lane = head c (zeros for the 8 padding heads),
-    // 8 consecutive dims 32 * kb + 8 * g of k-step kb.
+    // 8 consecutive dims 32 * kb + 8 * g of k-step kb.  Unconditional loads
+    // (padding lanes re-read head 0) so they issue with no branch between.
     bf16x8_t qb[8];
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (c < kG) w = *reinterpret_cast<const u32x4_t*>(p.q + (q_row + c) * kD + kb * 32 + g * 8);
-        qb[kb] = __builtin_bit_cast(bf16x8_t, w);
+        const int hq = c < kG ? c : 0;
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(p.q + (q_row + hq) * kD + kb * 32 +
+                                                           g * 8);
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        qb[kb] = __builtin_bit_cast(bf16x8_t, c < kG ? w : z);
     }
 
     f32x4_t O[16];   // O[head 4g + r][dim 16 nb + c]
@@ -147,15 +182,31 @@ __global__ __launch_bounds__(64 * kWaves, 1) void packed_kernel(const PackedPara
     const int32_t* blocks = p.tables + (int64_t)seq * p.table_stride;
     const uint16_t* kbase = p.k + (int64_t)kvh * p.kvh_s;
     const uint16_t* vbase = p.v + (int64_t)kvh * p.kvh_s;
-    const int tiles = (L + kTile - 1) / kTile;
+    // t_begin is a block boundary, and blocks hold whole tiles
+    const int t_first = t_begin / kTile;
+    const int t_last = (t_end + kTile - 1) / kTile;
 
-    for (int t = wave; t < tiles; t += kWaves) {
+    // Block ids of the range in windows of 64 (lane i: block b_lo + wbase +
+    // i), the next window requested one window ahead, so a tile reads its
+    // block id from a register instead of waiting on a table load.
+    const int b_lo = t_begin / p.bs;
+    const int nbk = t_end > t_begin ? (t_end - 1) / p.bs - b_lo + 1 : 0;   // blocks in range
+    int wbase = 0;
+    int bw = lane < nbk ? blocks[b_lo + lane] : -1;
+    int bw_next = lane + 64 < nbk ? blocks[b_lo + 64 + lane] : -1;
+
+    for (int t = t_first + wave; t < t_last; t += kWaves) {
         const int tok0 = t * kTile;
         const int b = tok0 / p.bs;
         const int slot0 = tok0 - b * p.bs;
-        const int blk = blocks[b];
+        while (b - b_lo - wbase >= 64) {   // wave-uniform; once per 64 blocks
+            wbase += 64;
+            bw = bw_next;
+            bw_next = lane + wbase + 64 < nbk ? blocks[b_lo + wbase + 64 + lane] : -1;
+        }
+        const int blk = __builtin_amdgcn_readlane(bw, b - b_lo - wbase);
         if ((uint32_t)blk >= p.num_blocks) continue;  // dropped: never dereferenced
-        const int nvalid = min(kTile, L - tok0);
+        const int nvalid = min(kTile, t_end - tok0);
         const uint16_t* kblk = kbase + (int64_t)blk * p.blk_s + (int64_t)slot0 * p.tok_s;
         const uint16_t* vblk = vbase + (int64_t)blk * p.blk_s + (int64_t)slot0 * p.tok_s;
 
@@ -267,8 +318,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void packed_kernel(const PackedPara
                 o0 += wt * ow[(w * kG + h) * 128 + d2];
                 o1 += wt * ow[(w * kG + h) * 128 + d2 + 1];
             }
-            const uint32_t v = Lsum > 0.f ? pack_bf16x2(o0 / Lsum, o1 / Lsum) : 0u;
-            *reinterpret_cast<uint32_t*>(p.out + (q_row + h) * kD + half * 128 + d2) = v;
+            if constexpr (SPLIT) {
+                float* slot = p.ws + ((q_row + h) * p.nsplit + sp) * (int64_t)(kD + 2);
+                if (Lsum > 0.f)
+                    *reinterpret_cast<float2*>(slot + half * 128 + d2) = make_float2(o0, o1);
+                if (half == 0 && d2 == 0) {
+                    slot[kD] = M * kLn2;
+                    slot[kD + 1] = Lsum;
+                }
+            } else {
+                const uint32_t v = Lsum > 0.f ? pack_bf16x2(o0 / Lsum, o1 / Lsum) : 0u;
+                *reinterpret_cast<uint32_t*>(p.out + (q_row + h) * kD + half * 128 + d2) = v;
+            }
         }
         __syncthreads();
     }
@@ -278,8 +339,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void packed_kernel(const PackedPara
 
 hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream) {
     const size_t lds = sizeof(uint16_t) * (size_t)kWaves * kVTileElems;   // 64 KiB
-    hipLaunchKernelGGL(packed_kernel, dim3((uint32_t)p.nkv, num_seqs), dim3(64 * kWaves), lds,
-                       stream, p);
+    if (p.nsplit > 1)
+        hipLaunchKernelGGL(packed_kernel<true>, dim3((uint32_t)(p.nkv * p.nsplit), num_seqs),
+                           dim3(64 * kWaves), lds, stream, p);
+    else
+        hipLaunchKernelGGL(packed_kernel<false>, dim3((uint32_t)p.nkv, num_seqs),
+                           dim3(64 * kWaves), lds, stream, p);
     return hipGetLastError();
 }
 

@@ -55,18 +55,21 @@ hipError_t launch_tiled_begin(float* m, float* l, float* o, uint64_t n_q, int he
 hipError_t launch_tiled_finalize(const float* l, const float* o, uint16_t* out, uint64_t n_q,
                                  int head_dim, hipStream_t stream);
 
-// GQA-packed MFMA decode (8 q heads x head_dim 256 per workgroup, one split).
+// GQA-packed MFMA decode (8 q heads x head_dim 256 per workgroup): one
+// split writes bf16 out; nsplit > 1 writes split-K partials to ws.
 struct PackedParams {
     const uint16_t* q;
     const uint16_t* k;
     const uint16_t* v;
     const int32_t* tables;
     const int32_t* lens;
-    uint16_t* out;
+    uint16_t* out;           // nsplit == 1
+    float* ws;               // nsplit > 1
     int64_t blk_s, tok_s, kvh_s;
     uint32_t num_blocks;
     int nq, nkv;
     int bs, table_stride;
+    int nsplit;
     float c;                 // scale * log2(e)
 };
 hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream);

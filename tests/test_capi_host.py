@@ -113,11 +113,17 @@ def test_decode_rejects_bad_arguments(bad):
 
 
 def test_packed_not_applicable_launches_nothing():
-    # shape outside the packed gate, or more than one split
+    # shapes outside the packed gate, with one split or several
     assert _decode(flags=P.PDA_DECODE_PACKED) == P.PDA_NOT_APPLICABLE
-    assert _decode(flags=P.PDA_DECODE_PACKED, num_q_heads=32, num_kv_heads=4, head_dim=256,
+    assert _decode(flags=P.PDA_DECODE_PACKED, num_q_heads=32, num_kv_heads=4, head_dim=128,
                    num_splits=2) == P.PDA_NOT_APPLICABLE
+    assert _decode(flags=P.PDA_DECODE_PACKED, num_q_heads=24, num_kv_heads=4, head_dim=256,
+                   num_splits=1) == P.PDA_NOT_APPLICABLE
     assert "not applicable" in P.pda_last_error()
+    assert P.pda_splitk_partials(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10**9, 2, 8, 2, 128, 16, 8,
+                                 32, 0.1, 2, P.PDA_DECODE_PACKED, 0) == P.PDA_NOT_APPLICABLE
+    with pytest.raises(P.PdaError):
+        _decode(flags=3)
 
 
 def test_empty_batch_is_a_no_op():
@@ -132,7 +138,7 @@ def test_merge_and_partials_validation():
         P.pda_splitk_merge(FAKE, 10**9, FAKE, 2, 8, 100, 4, 0)    # head dim
     with pytest.raises(P.PdaError):
         P.pda_splitk_partials(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10**9, 2, 8, 2, 128, 16, 8, 32,
-                              0.1, 1, 0)                          # partials need >= 2 splits
+                              0.1, 1, 0, 0)                       # partials need >= 2 splits
 
 
 def test_tiled_validate():

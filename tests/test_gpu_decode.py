@@ -179,6 +179,36 @@ def test_packed_mfma_workload():
         assert np.array_equal(host_bits(one)[0], full[s]), f"packed seq {s} differs alone"
 
 
+def test_packed_split_k_workload():
+    """The packed kernel's split-K form (this library's extension) at the Auto
+    split count on the packed workload: sampled rows against the oracle, the
+    workspace m / l of two rows against the oracle's split partials, and
+    batch invariance."""
+    inp = W.make_paged("packed", canary=True)
+    n = P.pda_auto_splits(CU, inp.num_q_heads)
+    say(f"[packed split-K] splits={n}")
+    dev = PagedOnDevice(inp)
+    rc, out, ws = dev.run(n, packed=True)
+    assert rc == P.PDA_OK
+    rows = [0, 1, 17, 40, 63]
+    sub = W.subset_paged(inp, rows)
+    ref, _, _ = A.paged_decode(sub.q, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens,
+                               sub.scale)
+    assert_out_close(host_bf16(out)[rows], ref, "packed split-K")
+    S, nq, D = inp.num_seqs, inp.num_q_heads, inp.head_dim
+    wsn = ws.cpu().numpy().reshape(S, nq, n, D + 2).astype(np.float64)
+    prow = [1, 40]
+    psub = W.subset_paged(inp, prow)
+    po, pm, pl = A.split_partials(psub.q, psub.k_cache, psub.v_cache, psub.block_tables,
+                                  psub.seq_lens, psub.scale, n)
+    assert_ml_close(wsn[prow][..., D], pm, "packed workspace m")
+    assert_ml_close(wsn[prow][..., D + 1], pl, "packed workspace l")
+    full = host_bits(out)
+    for s in (0, 40):
+        _, one, _ = dev.run(n, packed=True, rows=[s])
+        assert np.array_equal(host_bits(one)[0], full[s]), f"packed split-K seq {s} differs alone"
+
+
 @pytest.mark.parametrize("bs", [16, 32])
 def test_packed_mfma_edges(bs):
     lens = (0, 1, 15, 16, 17, 100, 333)
@@ -193,9 +223,13 @@ def test_packed_mfma_edges(bs):
                                inp.scale)
     assert_out_close(host_bf16(out), ref, "packed edges")
     assert np.all(host_bits(out)[0] == 0)
-    # the packed gate: other shapes or a split launch are not applicable
-    rc, _, _ = dev.run(2, packed=True)
-    assert rc == P.PDA_NOT_APPLICABLE
+    # the split-K form: same workspace partials as the oracle's splits, merged
+    for n in (2, 5, 16):
+        rc, out_n, ws = dev.run(n, packed=True)
+        assert rc == P.PDA_OK
+        assert_out_close(host_bf16(out_n), ref, f"packed split-K n={n}")
+        assert np.all(host_bits(out_n)[0] == 0)
+        _check_partials(dev, ws, n)
 
 
 def test_legacy_negative_control():
