@@ -90,6 +90,94 @@ def cpu_baseline(inp, seconds):
     return el / reps, reps
 
 
+def tiled_bench(args, K):
+    """The tiled state API on the scratch-pool workload: a step is
+    begin_step, every step_tile call of the plan_tiles schedule, finalize.
+    Returns the JSON record (without cpu_baseline)."""
+    import numpy as np
+    import torch
+
+    import paged_decode_attention_splitk_amd as P
+    import workloads as W
+
+    sc = W.make_scratch(args.workload, canary=False)
+    S, nq, D = sc.q.shape
+    nkv, bs, cap = sc.num_kv_heads, sc.block_size, sc.workload.tile_capacity
+    lens = sc.seq_lens.astype(np.int64)
+    calls = P.plan_tiles([sc.slot_tables[s] for s in range(S)], [int(x) for x in lens], bs, cap)
+    q = torch.from_numpy(np.ascontiguousarray(sc.q).view(np.int16)).cuda()
+    pool = torch.from_numpy(np.ascontiguousarray(sc.pool).view(np.int16)).cuda()
+    k_ptr = pool.data_ptr()
+    v_ptr = k_ptr + 2 * nkv * bs * D
+    dev_calls = [(torch.tensor(np.array(tb, np.int32).reshape(S, cap)).cuda(),
+                  torch.tensor(np.array(cnt, np.int32)).cuda(), lbvs) for tb, cnt, lbvs in calls]
+    out = torch.empty((S, nq, D), dtype=torch.int16, device="cuda")
+    h = P.TiledAttention(S, nq, nkv, D, bs, cap)
+    strides = h.scratch_pool_strides()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def tiles(_i=0):
+        for tb, cnt, lbvs in dev_calls:
+            h.step_tile(q, k_ptr, v_ptr, sc.num_slots, tb, cnt, S, strides, lbvs, stream=sp)
+
+    def step(_i=0):
+        h.begin_step(S, stream=sp)
+        tiles()
+        h.finalize(out, S, stream=sp)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(K):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K, (time.perf_counter() - t0) * 1e3 / K
+
+    gpu_ms, ms_per_step = timed(step)
+    tiles_ms, _ = timed(tiles)
+    # algorithmic bytes: valid K/V once; per active (call, sequence) its q,
+    # its tile-table entries and a read + write of its (m, l, o) state; the
+    # fill pass writes the state, finalize reads l, o and writes out
+    kv = int(lens.sum()) * nkv * D * 2 * 2
+    state_slot = nq * (D + 2) * 4
+    tiles_b = kv
+    for tb, cnt, lbvs in calls:
+        active = [c for c in cnt if c > 0]
+        tiles_b += len(active) * (nq * D * 2 + 2 * state_slot + 4) + 4 * int(sum(active))
+    begin_b = S * state_slot
+    fin_b = S * nq * (D + 1) * 4 + S * nq * D * 2
+    step_b = tiles_b + begin_b + fin_b
+    value = step_b / (ms_per_step * 1e-3) / 1e9
+    achieved = tiles_b / (tiles_ms * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": sc.workload.description, "num_seqs": S, "num_q_heads": nq,
+                   "num_kv_heads": nkv, "head_dim": D, "block_size": bs, "tile_capacity": cap,
+                   "total_tokens": int(lens.sum()), "step_tile_calls": len(calls),
+                   "algorithmic_bytes_per_step": step_b},
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "gpu_event_us_per_step": round(gpu_ms * 1e3, 2),
+        "kernels_us": {"step_tile_all_calls": round(tiles_ms * 1e3, 2)},
+        "roofline": {"kernel": f"tiled fold (fold_kernel<2,{D},{min(nq // nkv, 8)}>), all calls",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_step": tiles_b},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +208,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev_cus = P.pda_device_cu_count(0)
+
+    if W.WORKLOADS[args.workload].layout == "scratch":
+        rec = tiled_bench(args, args.steps)
+        print(json.dumps(rec), flush=True)
+        return
 
     inp = W.make_paged(args.workload, canary=False)
     S, nq, D = inp.q.shape

@@ -41,7 +41,7 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr int kD = 256;            // packed head dim
 constexpr int kG = 8;              // packed query heads per KV head
 constexpr int kTile = 16;          // tokens per tile
-constexpr int kWaves = 8;          // waves per workgroup
+constexpr int kWaves = 8;          // waves per workgroup, non-split form
 constexpr int kVTileElems = kTile * kD;   // one wave's V tile in LDS (8 KiB)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -128,8 +128,8 @@ __device__ __forceinline__ void packed_seq_of_rank(const int32_t* __restrict__ l
 
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <bool SPLIT>
-__global__ __launch_bounds__(64 * kWaves, 1) void packed_kernel(const PackedParams p) {
+template <bool SPLIT, int W>
+__global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p) {
     extern __shared__ __align__(16) uint16_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void packed_kernel(const PackedPara
     int bw = lane < nbk ? blocks[b_lo + lane] : -1;
     int bw_next = lane + 64 < nbk ? blocks[b_lo + 64 + lane] : -1;
 
-    for (int t = t_first + wave; t < t_last; t += kWaves) {
+    for (int t = t_first + wave; t < t_last; t += W) {
         const int tok0 = t * kTile;
         const int b = tok0 / p.bs;
         const int slot0 = tok0 - b * p.bs;
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void packed_kernel(const PackedPara
     // real head m and l, then o for one half of the dims at a time.
     __syncthreads();
     float* ml = reinterpret_cast<float*>(smem);                 // [W][8][2]
-    float* ow = ml + kWaves * kG * 2;                           // [W][8][128]
+    float* ow = ml + W * kG * 2;                           // [W][8][128]
     if (g == 0 && c < kG) {
         ml[(wave * kG + c) * 2] = m;
         ml[(wave * kG + c) * 2 + 1] = l;
@@ -306,13 +306,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void packed_kernel(const PackedPara
                     ow[(wave * kG + 4 * g + r) * 128 + nb * 16 + c] = O[half * 8 + nb][r];
         }
         __syncthreads();
-        for (int i = tid; i < kG * 64; i += 64 * kWaves) {
+        for (int i = tid; i < kG * 64; i += 64 * W) {
             const int h = i / 64, d2 = (i % 64) * 2;     // two dims of this half
             float M = kNegInf;
-            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[(w * kG + h) * 2]);
+            for (int w = 0; w < W; ++w) M = fmaxf(M, ml[(w * kG + h) * 2]);
             const float Ms = M == kNegInf ? 0.f : M;
             float Lsum = 0.f, o0 = 0.f, o1 = 0.f;
-            for (int w = 0; w < kWaves; ++w) {
+            for (int w = 0; w < W; ++w) {
                 const float wt = fexp2(ml[(w * kG + h) * 2] - Ms);
                 Lsum += wt * ml[(w * kG + h) * 2 + 1];
                 o0 += wt * ow[(w * kG + h) * 128 + d2];
@@ -338,13 +338,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void packed_kernel(const PackedPara
 }  // namespace
 
 hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream) {
-    const size_t lds = sizeof(uint16_t) * (size_t)kWaves * kVTileElems;   // 64 KiB
-    if (p.nsplit > 1)
-        hipLaunchKernelGGL(packed_kernel<true>, dim3((uint32_t)(p.nkv * p.nsplit), num_seqs),
+    if (p.nsplit > 1) {
+        // A split holds about 1/nsplit of a sequence: the more splits, the
+        // fewer tiles each item has, and the fewer waves pay off (measured
+        // on 64 sequences of 1K-8K tokens: 2 waves best at 16 splits, 4 at
+        // 4-8, 8 at 2).  Results do not depend on the wave count choice
+        // beyond the order of the final in-workgroup merge.
+        const dim3 grid((uint32_t)(p.nkv * p.nsplit), num_seqs);
+        const int w = p.nsplit >= 12 ? 2 : (p.nsplit >= 3 ? 4 : 8);
+        const size_t lds = sizeof(uint16_t) * (size_t)w * kVTileElems;
+        if (w == 2)
+            hipLaunchKernelGGL((packed_kernel<true, 2>), grid, dim3(128), lds, stream, p);
+        else if (w == 4)
+            hipLaunchKernelGGL((packed_kernel<true, 4>), grid, dim3(256), lds, stream, p);
+        else
+            hipLaunchKernelGGL((packed_kernel<true, 8>), grid, dim3(512), lds, stream, p);
+    } else {
+        const size_t lds = sizeof(uint16_t) * (size_t)kWaves * kVTileElems;   // 64 KiB
+        hipLaunchKernelGGL((packed_kernel<false, kWaves>), dim3((uint32_t)p.nkv, num_seqs),
                            dim3(64 * kWaves), lds, stream, p);
-    else
-        hipLaunchKernelGGL(packed_kernel<false>, dim3((uint32_t)p.nkv, num_seqs),
-                           dim3(64 * kWaves), lds, stream, p);
+    }
     return hipGetLastError();
 }
 
