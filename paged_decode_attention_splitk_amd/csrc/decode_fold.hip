@@ -87,6 +87,44 @@ __device__ __forceinline__ float nsum(float x) {
     return x;
 }
 
+// Values of the two lanes 16 apart (rows 2i and 2i + 1 of 16 lanes) and of
+// the two lanes 32 apart (the wave's halves), identical on both partners.
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+// Max / sum over the 64 / LPT token rows of a wave (lanes LPT apart), in a
+// fixed butterfly order; every lane gets identical bits.
+template <int LPT>
+__device__ __forceinline__ float rows_max(float x) {
+    float a, b;
+    if constexpr (LPT <= 8) x = fmaxf(x, dpp<0x128>(x));   // row_ror:8, lanes 8 apart
+    if constexpr (LPT <= 16) {
+        swap16(x, a, b);
+        x = fmaxf(a, b);
+    }
+    swap32(x, a, b);
+    return fmaxf(a, b);
+}
+template <int LPT>
+__device__ __forceinline__ float rows_sum(float x) {
+    float a, b;
+    if constexpr (LPT <= 8) x = x + dpp<0x128>(x);
+    if constexpr (LPT <= 16) {
+        swap16(x, a, b);
+        x = a + b;
+    }
+    swap32(x, a, b);
+    return a + b;
+}
+
 // Orders this wave's LDS accesses: the writes before it are complete, and
 // visible to every lane of the wave, before the reads after it.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -158,6 +196,10 @@ __device__ __forceinline__ void seq_of_rank(const int32_t* __restrict__ lens, in
 #ifndef PDA_FOLD_PV_BF16
 #define PDA_FOLD_PV_BF16 0
 #endif
+
+// Workgroups of at least this many waves merge each wave's token rows in
+// registers before the LDS merge (see the epilogue).
+constexpr int kRowMergeWaves = 4;
 
 // Lane layout of the fold for head_dim D and GC heads per workgroup.
 template <int D, int GC>
@@ -438,29 +480,73 @@ __global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
         wave_lds_sync();  // the next group's partials overwrite this scratch
     }
 
-    // Every (wave, row) state -> LDS, then one fixed-order merge.  Layout
-    // (aliasing the loop scratch): o [NC][GC][D], m [NC][GC], l [NC][GC],
-    // weights [NC + 1][GC], L [GC], with NC = waves * ROWS contributors.
-    const int NC = nw * ROWS;
+    // Wave epilogue, then every contributor's state goes to LDS and one
+    // fixed-order pass merges them.  Layout (aliasing the loop scratch):
+    // o [NC][GC][D], m [NC][GC], l [NC][GC], weights [NC + 1][GC], L [GC].
+    //  * nw < kRowMergeWaves: each (wave, row) state is a contributor,
+    //    NC = nw * ROWS (cheapest for few waves).
+    //  * otherwise the wave's ROWS row states merge first, with cross-lane
+    //    reductions over the rows (a fixed butterfly, so every lane ends
+    //    with the same bits): per head, the row's m and l are broadcast to
+    //    the row's lanes, M = max over rows, w = exp(m - M), and l and o are
+    //    summed with weight w; NC = nw, which keeps the LDS small enough for
+    //    wide workgroups.
+    const bool row_merge = nw >= kRowMergeWaves;
+    const int NC = row_merge ? nw : nw * ROWS;
     float* eo = lds;
     float* em = eo + NC * GC * D;
     float* el = em + NC * GC;
     float* ew = el + NC * GC;
     float* eL = ew + (NC + 1) * GC;
-    const int ci = wave * ROWS + row;
-    __syncthreads();
+    if (row_merge) {
+        float wM[GC], wL[GC];   // per head, identical in every lane of the wave
 #pragma unroll
-    for (int h = 0; h < GC; ++h) {
-        float* dst = eo + (ci * GC + h) * D + sub * 8;
-        *reinterpret_cast<f32x4*>(dst) = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
-        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
-    }
+        for (int h = 0; h < GC; ++h) {
+            const int j = h * U;                        // the head's first score pair
+            const int src = (row * LPT + j % LPT) * 4;  // its owner in this row (bytes)
+            const float mr =
+                __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(m[j / LPT])));
+            const float lr =
+                __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(l[j / LPT])));
+            const float M = rows_max<LPT>(mr);
+            const float w = fexp2(mr - (M == kNegInf ? 0.f : M));
+            wM[h] = M;
+            wL[h] = rows_sum<LPT>(w * lr);
 #pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-        const int j = sub + LPT * k;
-        if (j < NP && j % U == 0) {
-            em[ci * GC + j / U] = m[k];
-            el[ci * GC + j / U] = l[k];
+            for (int d = 0; d < 8; ++d) o[h][d] = rows_sum<LPT>(w * o[h][d]);
+        }
+        __syncthreads();
+        if (row == 0) {
+#pragma unroll
+            for (int h = 0; h < GC; ++h) {
+                float* dst = eo + (wave * GC + h) * D + sub * 8;
+                *reinterpret_cast<f32x4*>(dst) = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+                *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < GC; ++h) {
+            if (lane == h) {
+                em[wave * GC + h] = wM[h];
+                el[wave * GC + h] = wL[h];
+            }
+        }
+    } else {
+        const int ci = wave * ROWS + row;
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < GC; ++h) {
+            float* dst = eo + (ci * GC + h) * D + sub * 8;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[h][4], o[h][5], o[h][6], o[h][7]};
+        }
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+            const int j = sub + LPT * k;
+            if (j < NP && j % U == 0) {
+                em[ci * GC + j / U] = m[k];
+                el[ci * GC + j / U] = l[k];
+            }
         }
     }
     __syncthreads();
@@ -674,7 +760,7 @@ FoldFn pick_d(int D, int gc) {
 template <int D, int GC>
 size_t fold_lds_floats(int waves) {
     using S = FoldShape<D, GC>;
-    const size_t nc = (size_t)waves * S::ROWS;
+    const size_t nc = (size_t)(waves >= kRowMergeWaves ? waves : waves * S::ROWS);
     const size_t epi = nc * GC * D + 2 * nc * GC + (nc + 1) * GC + GC;
     const size_t loop = (size_t)waves * S::WAVE_FLOATS;
     return epi > loop ? epi : loop;
