@@ -14,6 +14,10 @@
 #include <cstring>
 #include <string>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "pda.h"
 #include "pda_geometry.h"
 #include "pda_kernels.h"
@@ -49,6 +53,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // Head groups of one KV head: G q heads in groups of at most 8, as even as
 // possible.  Returns the group width; *hg receives the group count.
+// Head groups per KV head (at most kMaxHeadsPerGroup heads each, so every
+// K/V byte serves as many heads as one workgroup holds) and heads per group.
 int head_groups(uint32_t G, int* hg) {
     const int groups = (int)((G + pda::kMaxHeadsPerGroup - 1) / pda::kMaxHeadsPerGroup);
     *hg = groups;
@@ -63,10 +69,36 @@ int head_groups(uint32_t G, int* hg) {
 #ifndef PDA_ONESHOT_WAVES_WIDE
 #define PDA_ONESHOT_WAVES_WIDE 2
 #endif
-int oneshot_waves(uint32_t nkv, int hg, uint32_t nsplit, uint32_t head_dim, int gc) {
-    const uint64_t per_seq = (uint64_t)nkv * hg * nsplit;
-    int w = per_seq >= 128 ? PDA_ONESHOT_WAVES_WIDE : 8;
-    while (w > 1 && pda::fold_lds_bytes((int)head_dim, gc, w) > 64 * 1024) --w;
+
+// LDS bytes one workgroup may use on the current device (64 KiB if the
+// runtime does not say), cached per device.
+size_t lds_per_block() {
+    static std::mutex mu;
+    static std::vector<std::pair<int, size_t>> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 64 * 1024;
+    std::lock_guard<std::mutex> g(mu);
+    for (const auto& c : cache)
+        if (c.first == dev) return c.second;
+    int v = 0;
+    size_t bytes = 64 * 1024;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+        v > 0)
+        bytes = (size_t)v;
+    cache.emplace_back(dev, bytes);
+    return bytes;
+}
+
+// Whether a one-shot launch gives each sequence few workgroups (fewer than
+// 128 (KV head, split) items): such launches get the widest workgroups the
+// kernel allows (12 waves up to 6 heads per group, else 8), within the
+// device's LDS per workgroup.
+bool few_items(uint32_t nkv, uint32_t nsplit) { return (uint64_t)nkv * nsplit < 128; }
+
+int oneshot_waves(uint32_t nkv, uint32_t nsplit, uint32_t head_dim, int gc) {
+    int w = few_items(nkv, nsplit) ? pda::fold_max_waves(gc) : PDA_ONESHOT_WAVES_WIDE;
+    const size_t cap = lds_per_block();
+    while (w > 1 && pda::fold_lds_bytes((int)head_dim, gc, w) > cap) --w;
     return w;
 }
 
@@ -174,7 +206,7 @@ int run_partials(const DecodeShape& s, const void* q, const void* k, const void*
     const int gc = head_groups(s.nq / s.nkv, &hg);
     pda::FoldParams p = fold_params(s, q, k, v, bt, lens, hg, scale, nsplit);
     p.ws = ws;
-    const int waves = oneshot_waves(s.nkv, hg, nsplit, s.D, gc);
+    const int waves = oneshot_waves(s.nkv, nsplit, s.D, gc);
     const uint64_t gx = (uint64_t)s.nkv * hg * nsplit;
     hipError_t e = pda::launch_fold(pda::kModePartial, (int)s.D, gc, p, (uint32_t)gx, s.num_seqs,
                                     waves, stream);
@@ -290,7 +322,7 @@ int pda_paged_decode(const void* q, const void* k_cache, const void* v_cache,
         pda::FoldParams p =
             fold_params(s, q, k_cache, v_cache, block_tables, seq_lens, hg, scale, 1);
         p.out = static_cast<uint16_t*>(out);
-        const int waves = oneshot_waves(num_kv_heads, hg, 1, head_dim, gc);
+        const int waves = oneshot_waves(num_kv_heads, 1, head_dim, gc);
         hipError_t e = pda::launch_fold(pda::kModeFinal, (int)head_dim, gc, p,
                                         (uint32_t)(num_kv_heads * hg), num_seqs, waves, st);
         if (e != hipSuccess) return hip_fail(e, "single-split decode launch");

@@ -38,6 +38,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "pda_geometry.h"
 #include "pda_kernels.h"
 
@@ -219,8 +223,12 @@ struct FoldShape {
     static_assert(LPT % U == 0, "a head's scores sit in aligned lane sets");
 };
 
+// Largest workgroup of the fold for GC heads: 12 waves up to 6 heads (3 waves
+// per SIMD fit their registers), 8 beyond.
+__host__ __device__ constexpr int fold_max_threads(int gc) { return gc <= 6 ? 768 : 512; }
+
 template <int MODE, int D, int GC>
-__global__ __launch_bounds__(512) void fold_kernel(const FoldParams p) {
+__global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldParams p) {
     using S = FoldShape<D, GC>;
     constexpr int LPT = S::LPT, ROWS = S::ROWS, U = S::U, TG = S::TG, NP = S::NP,
                   NP4 = S::NP4, PPL = S::PPL, TS = S::TS, TROW = S::TROW, XS = S::XS;
@@ -803,11 +811,28 @@ hipError_t launch_fold(int mode, int head_dim, int gc, const FoldParams& p, uint
         case kModeTiled: fn = pick_d<kModeTiled>(head_dim, gc); break;
         default: break;
     }
-    if (!fn) return hipErrorInvalidValue;
+    if (!fn || waves < 1 || 64 * waves > fold_max_threads(gc)) return hipErrorInvalidValue;
     const size_t lds = fold_lds_bytes(head_dim, gc, waves);
+    if (lds > 64 * 1024) {
+        // dynamic LDS past 64 KiB is requested per kernel, once
+        static std::mutex mu;
+        static std::vector<std::pair<FoldFn, size_t>> granted;
+        std::lock_guard<std::mutex> g(mu);
+        bool have = false;
+        for (const auto& e : granted) have |= e.first == fn && e.second >= lds;
+        if (!have) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds);
+            if (e != hipSuccess) return e;
+            granted.emplace_back(fn, lds);
+        }
+    }
     hipLaunchKernelGGL(fn, dim3(grid_x, grid_y), dim3(64 * waves), lds, stream, p);
     return hipGetLastError();
 }
+
+int fold_max_waves(int gc) { return fold_max_threads(gc) / 64; }
 
 hipError_t launch_merge(const float* ws, uint16_t* out, uint32_t num_seqs, int nq, int head_dim,
                         int nsplit, hipStream_t stream) {

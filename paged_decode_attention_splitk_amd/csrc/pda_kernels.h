@@ -40,6 +40,9 @@ constexpr int kMaxHeadsPerGroup = 8;
 // LDS bytes a fold workgroup of `waves` waves needs.
 size_t fold_lds_bytes(int head_dim, int gc, int waves);
 
+// Most waves a fold workgroup for gc heads may have (its launch bound).
+int fold_max_waves(int gc);
+
 // Launches the fold kernel for (mode, head_dim, gc) on grid x = `grid_x`,
 // y = number of sequences.  head_dim in {64, 128, 256}, gc in 1..8.
 hipError_t launch_fold(int mode, int head_dim, int gc, const FoldParams& p, uint32_t grid_x,
