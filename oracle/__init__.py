@@ -14,6 +14,7 @@ Contents
                       partials, tiled running state).
 ``oracle.geometry``   the launch-geometry formulas of the attn_splitk module
                       page, written out in Python integers.
+``oracle.prefill``    causal paged prefill (the prefill page's kernel), FP64.
 ``oracle.policy``     that page's policy grammar and resolution rules
                       (parse, parse_gqa_pack, resolve_policy,
                       resolve_gqa_pack).

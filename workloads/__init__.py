@@ -74,8 +74,10 @@ class Workload:
     len_range: tuple | None = None         # (lo, hi) inclusive
     forced: tuple = ()                     # ((index, length), ...)
     pool_blocks: int | None = None         # fixed pool size (else = total needed)
-    layout: str = "paged"                  # "paged" or "scratch"
+    layout: str = "paged"                  # "paged", "scratch" or "prefill"
     tile_capacity: int = 0                 # tiled API only
+    q_len: int = 0                         # prefill only: query rows
+    q_offset: int = 0                      # prefill only: position of query row 0
     description: str = ""
 
 
@@ -108,6 +110,20 @@ WORKLOADS = {
         description="128 seqs, lengths U[0, 16384] plus forced edge lengths, "
                     "16 q / 4 kv heads, D 256, block 32, scratch-pool layout, "
                     "64 blocks per tile"),
+    # causal prefill of one sequence (the prefill page's 128-row kernel shape:
+    # head dim 256, GQA, paged BF16 cache)
+    "prefill": Workload(
+        name="prefill", seed=5, num_seqs=1, num_q_heads=32, num_kv_heads=4,
+        head_dim=256, block_size=16, seq_lens=(4096,), layout="prefill",
+        q_len=4096, q_offset=0,
+        description="causal prefill of one 4096-token sequence, 32 q / 4 kv heads, "
+                    "D 256, block 16, shuffled pool"),
+    "prefill_chunk": Workload(
+        name="prefill_chunk", seed=6, num_seqs=1, num_q_heads=32, num_kv_heads=4,
+        head_dim=256, block_size=16, seq_lens=(8192,), layout="prefill",
+        q_len=2048, q_offset=6144,
+        description="chunked causal prefill: the last 2048 of 8192 tokens, 32 q / "
+                    "4 kv heads, D 256, block 16, shuffled pool"),
 }
 
 
@@ -303,3 +319,73 @@ def subset_paged(inp: PagedInputs, seqs) -> PagedInputs:
     return PagedInputs(inp.workload, np.ascontiguousarray(inp.q[seqs]), inp.k_cache, inp.v_cache,
                        np.ascontiguousarray(inp.block_tables[seqs]),
                        np.ascontiguousarray(inp.seq_lens[seqs]), inp.scale)
+
+
+@dataclasses.dataclass
+class PrefillInputs:
+    """Causal prefill inputs for one sequence (host numpy arrays).
+
+    q            uint16 [q_len, num_q_heads, head_dim]   (BF16 bits); row i
+                 is the token at position q_offset + i
+    k_cache      uint16 [num_blocks, block_size, num_kv_heads, head_dim]
+    v_cache      uint16 [num_blocks, block_size, num_kv_heads, head_dim]
+    block_table  int32  [max_blocks]   (-1 = unused)
+    kv_len       tokens of K / V in the cache for this sequence
+    scale        float  (an FP32 value, 1/sqrt(head_dim))
+    """
+    workload: Workload
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_table: np.ndarray
+    kv_len: int
+    q_offset: int
+    scale: float
+
+    @property
+    def q_len(self): return self.q.shape[0]
+    @property
+    def num_q_heads(self): return self.q.shape[1]
+    @property
+    def head_dim(self): return self.q.shape[2]
+    @property
+    def num_kv_heads(self): return self.k_cache.shape[2]
+    @property
+    def block_size(self): return self.k_cache.shape[1]
+    @property
+    def num_blocks(self): return self.k_cache.shape[0]
+
+
+def make_prefill(w: Workload | str, canary: bool = True, q_len: int | None = None,
+                 kv_len: int | None = None, q_offset: int | None = None) -> PrefillInputs:
+    """Generate causal-prefill inputs: the sequence's K / V follow the paged
+    recipe above (steps 1-3, 5-7) with ``kv_len`` tokens; then the queries,
+    ``rng.standard_normal((q_len, num_q_heads, head_dim), float32)``, are
+    drawn after the block permutation.  ``q_len`` / ``kv_len`` / ``q_offset``
+    override the workload's values."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    assert w.layout == "prefill"
+    kv = int(w.seq_lens[0] if kv_len is None else kv_len)
+    ql = int(w.q_len if q_len is None else q_len)
+    qo = int(w.q_offset if q_offset is None else q_offset)
+    w = dataclasses.replace(w, seq_lens=(kv,), q_len=ql, q_offset=qo)
+    rng = np.random.default_rng(w.seed)
+    lens = _draw_lens(w, rng)
+    bs, nkv, D, nq = w.block_size, w.num_kv_heads, w.head_dim, w.num_q_heads
+    nblk, pool_blocks, tables = _layout(w, rng, lens, bs)
+    q = f32_to_bf16_bits(rng.standard_normal((ql, nq, D), dtype=np.float32))
+    fill = BF16_QNAN if canary else np.uint16(0)
+    k_cache = np.full((max(pool_blocks, 1), bs, nkv, D), fill, dtype=np.uint16)
+    v_cache = np.full((max(pool_blocks, 1), bs, nkv, D), fill, dtype=np.uint16)
+    n = int(nblk[0])
+    if n:
+        k, v = _seq_kv(w.seed, 0, n, bs, nkv, D)
+        tail = kv - (n - 1) * bs
+        if canary and tail < bs:
+            k[n - 1, tail:] = BF16_QNAN
+            v[n - 1, tail:] = BF16_QNAN
+        k_cache[tables[0, :n]] = k
+        v_cache[tables[0, :n]] = v
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    return PrefillInputs(w, q, k_cache, v_cache, tables[0].copy(), kv, qo, scale)
