@@ -178,6 +178,64 @@ def tiled_bench(args, K):
     }
 
 
+def prefill_bench(args, K):
+    """Causal paged prefill of one sequence (pda_paged_prefill); reported in
+    TFLOP/s of the causal attention (q.k and P.V, 2 flops per multiply-add,
+    every unmasked (row, key) pair) against the bf16 MFMA peak."""
+    import numpy as np
+    import torch
+
+    import paged_decode_attention_splitk_amd as P
+    import workloads as W
+
+    pi = W.make_prefill(args.workload, canary=False)
+    ql, nq, D = pi.q.shape
+    nkv, bs = pi.num_kv_heads, pi.block_size
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    q, k, v = up(pi.q), up(pi.k_cache), up(pi.v_cache)
+    bt = torch.from_numpy(pi.block_table).cuda()
+    out = torch.empty((ql, nq, D), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(_i=0):
+        rc = P.pda_paged_prefill(q, k, v, out, bt, ql, pi.kv_len, pi.q_offset, nq, nkv, D, bs,
+                                 len(pi.block_table), pi.num_blocks, pi.scale, stream=sp)
+        assert rc == P.PDA_OK
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    gpu_ms = e0.elapsed_time(e1) / K
+    keys = np.minimum(pi.q_offset + np.arange(ql) + 1, pi.kv_len).astype(np.int64)
+    flops = 4.0 * nq * D * float(keys.sum())
+    tflops = flops / (gpu_ms * 1e-3) / 1e12
+    kv_bytes = pi.kv_len * nkv * D * 2 * 2
+    return {
+        "metric": "causal paged prefill TFLOP/s", "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": pi.workload.description, "q_len": ql, "kv_len": pi.kv_len,
+                   "q_offset": pi.q_offset, "num_q_heads": nq, "num_kv_heads": nkv,
+                   "head_dim": D, "block_size": bs, "flops_per_step": flops},
+        "us_per_step": round(ms * 1e3, 2), "gpu_event_us_per_step": round(gpu_ms * 1e3, 2),
+        "roofline": {"kernel": "causal prefill (prefill_kernel)", "bound": "mfma",
+                     "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "kv_bytes_per_step": kv_bytes},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +269,10 @@ def main():
 
     if W.WORKLOADS[args.workload].layout == "scratch":
         rec = tiled_bench(args, args.steps)
+        print(json.dumps(rec), flush=True)
+        return
+    if W.WORKLOADS[args.workload].layout == "prefill":
+        rec = prefill_bench(args, args.steps)
         print(json.dumps(rec), flush=True)
         return
 

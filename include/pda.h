@@ -126,6 +126,42 @@ uint64_t pda_gqa_pack_ctas(uint32_t num_kv_heads, uint32_t num_seqs);
 uint32_t pda_split_chunk(uint32_t seq_len, uint32_t num_splits, uint32_t block_size);
 
 /* ------------------------------------------------------------------------
+ * Causal paged prefill (prefill page "prefill_attn_fa128.rs": `applies` and
+ * the `paged` launcher; head dim 256, 128 query rows per workgroup).
+ * ------------------------------------------------------------------------ */
+
+/* Whether the prefill kernel serves a launch: head_dim == 256, causal,
+ * sliding_window == 0, num_kv_heads > 0 and num_q_heads % num_kv_heads == 0. */
+int pda_prefill_applies(uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                        int causal, uint32_t sliding_window);
+
+/* Causal attention of one sequence's q_len new rows over its paged cache.
+ *
+ *   q            bf16 [q_len, num_q_heads, head_dim]; row i is the token at
+ *                position q_offset + i
+ *   k_cache      bf16 [num_blocks, block_size, num_kv_heads, head_dim]
+ *   v_cache      bf16, same layout
+ *   out          bf16 [q_len, num_q_heads, head_dim]
+ *   block_table  int32 [max_blocks]: the sequence's pool blocks in token
+ *                order (entry j holds tokens [j*block_size, (j+1)*block_size))
+ *   kv_len       tokens of the sequence in the cache (<= max_blocks*block_size)
+ *   scale        multiplies q.k (the page's inv_sqrt_d)
+ * Row i attends the keys at positions j <= q_offset + i with j < kv_len;
+ * q head h reads KV head h / (num_q_heads / num_kv_heads); a row with no key
+ * is 0.  Returns PDA_NOT_APPLICABLE, launching nothing, when q_len == 0 or
+ * pda_prefill_applies(num_q_heads, num_kv_heads, head_dim, 1, sliding_window)
+ * is 0 (the caller runs another kernel); PDA_EINVAL for a bad argument.
+ * Requirements: block_size > 0, num_blocks > 0, q_offset + q_len and kv_len
+ * below 2^31, q / caches / out 16-byte aligned.  Block ids outside
+ * [0, num_blocks) give unspecified but in-bounds results.  Allocates nothing;
+ * asynchronous on `stream`. */
+int pda_paged_prefill(const void* q, const void* k_cache, const void* v_cache, void* out,
+                      const int32_t* block_table, uint32_t q_len, uint32_t kv_len,
+                      uint32_t q_offset, uint32_t num_q_heads, uint32_t num_kv_heads,
+                      uint32_t head_dim, uint32_t block_size, uint32_t max_blocks,
+                      uint32_t num_blocks, uint32_t sliding_window, float scale, void* stream);
+
+/* ------------------------------------------------------------------------
  * Policy resolution (attn_splitk page: parse, parse_gqa_pack,
  * resolve_policy, policy_from_env, resolve_gqa_pack, gqa_pack_enabled,
  * DECODE_GQA_PACK_DECLARED).  Host-only; no HIP calls.  Text is trimmed of

@@ -98,6 +98,9 @@ _SIGS = {
     "pda_splitk_merge": (_int, [_vp, _u64, _vp, _u32, _u32, _u32, _u32, _vp]),
     "pda_splitk_partials": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _u64, _u32, _u32, _u32, _u32,
                                    _u32, _u32, _u32, _f32, _u32, _u32, _vp]),
+    "pda_prefill_applies": (_int, [_u32, _u32, _u32, _int, _u32]),
+    "pda_paged_prefill": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _u32, _u32, _u32,
+                                 _u32, _u32, _u32, _u32, _f32, _vp]),
     "pda_tiled_validate": (_int, [ctypes.POINTER(pda_tiled_dims)]),
     "pda_tiled_create": (_int, [ctypes.POINTER(pda_tiled_dims), ctypes.POINTER(_vp)]),
     "pda_tiled_destroy": (None, [_vp]),
@@ -256,6 +259,21 @@ def pda_splitk_partials(q, k_cache, v_cache, block_tables, seq_lens, workspace,
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         _ptr(workspace), workspace_floats, num_seqs, num_q_heads, num_kv_heads, head_dim,
         block_size, max_blocks_per_seq, num_blocks, scale, num_splits, flags, _stream(stream)))
+
+
+# ---------------------------------------------------------------- prefill
+def pda_prefill_applies(num_q_heads, num_kv_heads, head_dim, causal=True, sliding_window=0):
+    return bool(_lib.pda_prefill_applies(num_q_heads, num_kv_heads, head_dim, int(bool(causal)),
+                                         sliding_window))
+
+
+def pda_paged_prefill(q, k_cache, v_cache, out, block_table, q_len, kv_len, q_offset,
+                      num_q_heads, num_kv_heads, head_dim, block_size, max_blocks, num_blocks,
+                      scale, sliding_window=0, stream=None) -> int:
+    return _check(_lib.pda_paged_prefill(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(block_table), q_len, kv_len,
+        q_offset, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks, num_blocks,
+        sliding_window, scale, _stream(stream)))
 
 
 # ---------------------------------------------------------------- tiled

@@ -256,6 +256,56 @@ int pda_splitk_partials(const void* q, const void* k_cache, const void* v_cache,
     return rc == PDA_OK ? ok() : rc;
 }
 
+int pda_prefill_applies(uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                        int causal, uint32_t sliding_window) {
+    return head_dim == 256 && causal && sliding_window == 0 && num_kv_heads > 0 &&
+           num_q_heads % num_kv_heads == 0;
+}
+
+int pda_paged_prefill(const void* q, const void* k_cache, const void* v_cache, void* out,
+                      const int32_t* block_table, uint32_t q_len, uint32_t kv_len,
+                      uint32_t q_offset, uint32_t num_q_heads, uint32_t num_kv_heads,
+                      uint32_t head_dim, uint32_t block_size, uint32_t max_blocks,
+                      uint32_t num_blocks, uint32_t sliding_window, float scale, void* stream) {
+    if (q_len == 0 ||
+        !pda_prefill_applies(num_q_heads, num_kv_heads, head_dim, 1, sliding_window)) {
+        g_last_error = "prefill kernel not applicable: needs q_len > 0, head_dim 256, causal, "
+                       "no sliding window and num_q_heads a multiple of num_kv_heads";
+        return PDA_NOT_APPLICABLE;
+    }
+    if (!q || !k_cache || !v_cache || !out || !block_table)
+        return fail(PDA_EINVAL, "null pointer argument");
+    if (block_size == 0 || num_blocks == 0 || max_blocks == 0)
+        return fail(PDA_EINVAL, "block_size, num_blocks and max_blocks must be positive");
+    if ((uint64_t)q_offset + q_len >= (1ull << 31) || kv_len >= (1u << 31))
+        return fail(PDA_EINVAL, "q_offset + q_len and kv_len must be below 2^31");
+    if ((uint64_t)kv_len > (uint64_t)max_blocks * block_size)
+        return fail(PDA_EINVAL, "kv_len %u exceeds the block table (%u blocks of %u)", kv_len,
+                    max_blocks, block_size);
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+        return fail(PDA_EINVAL, "q, caches and out must be 16-byte aligned");
+    if (!std::isfinite(scale)) return fail(PDA_EINVAL, "scale is not finite");
+    pda::PrefillParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k_cache);
+    p.v = static_cast<const uint16_t*>(v_cache);
+    p.table = block_table;
+    p.out = static_cast<uint16_t*>(out);
+    p.blk_s = (int64_t)block_size * num_kv_heads * head_dim;
+    p.tok_s = (int64_t)num_kv_heads * head_dim;
+    p.num_blocks = num_blocks;
+    p.nq = (int)num_q_heads;
+    p.nkv = (int)num_kv_heads;
+    p.bs = (int)block_size;
+    p.q_len = (int)q_len;
+    p.kv_len = (int)kv_len;
+    p.q_offset = (int)q_offset;
+    p.c = scale * kLog2e;
+    hipError_t e = pda::launch_prefill(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return ok();
+}
+
 int pda_splitk_merge(const float* workspace, uint64_t workspace_floats, void* out,
                      uint32_t num_seqs, uint32_t num_q_heads, uint32_t head_dim,
                      uint32_t num_splits, void* stream) {

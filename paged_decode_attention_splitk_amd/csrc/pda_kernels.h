@@ -77,4 +77,19 @@ struct PackedParams {
 };
 hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream);
 
+// Causal paged prefill of one sequence, head_dim 256 (MFMA).
+struct PrefillParams {
+    const uint16_t* q;       // bf16 [q_len, nq, 256]
+    const uint16_t* k;       // bf16 K pool
+    const uint16_t* v;       // bf16 V pool
+    const int32_t* table;    // block table of the sequence
+    uint16_t* out;           // bf16 [q_len, nq, 256]
+    int64_t blk_s, tok_s;    // element strides of the pools
+    uint32_t num_blocks;
+    int nq, nkv, bs;
+    int q_len, kv_len, q_offset;
+    float c;                 // scale * log2(e)
+};
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
 }  // namespace pda

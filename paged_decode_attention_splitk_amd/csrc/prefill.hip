@@ -1,0 +1,253 @@
+// Causal paged prefill attention on MFMA (gfx950), head_dim 256.
+//
+// The launch shape follows the prefill page ("metrale_model_layers/layers/
+// ops/prefill_attn_fa128.rs", the paged launcher and its constants): grid
+// [num_q_heads, ceil(q_len / 128)], 128 query rows per workgroup, K and V
+// tiles of 32 rows staged in LDS and read once per 128 rows, P kept in
+// registers, every wave doing both q.k and P.V.  Here a workgroup is 8 waves
+// of 16 query rows (wave64), and the arithmetic is laid out for CDNA4:
+//
+//   S^T[16 key][16 query] = K[16][256] . Q^T[256][16]
+//       8 x v_mfma_f32_16x16x32_bf16; K (A operand: lane = key, 8 dims) comes
+//       from the LDS tile, Q (B operand: lane = query) stays in registers.
+//   online softmax (FP32, base 2) on the accumulator: each query's 16
+//       scores sit in one column across the four 16-lane groups; the causal
+//       mask and the end of the cache turn scores into -inf there.
+//   O[16 query][256] += P[16][16] . V[16][256]
+//       16 x v_mfma_f32_16x16x16_bf16; the S^T accumulator is P in the
+//       A-operand layout, V comes back from LDS transposed by
+//       ds_read_b64_tr_b16.
+//
+// Query row i is the token at position q_offset + i and attends the keys at
+// positions j <= q_offset + i with j < kv_len.  K / V rows past kv_len, or in
+// a block whose id is outside the pool, are staged from key 0 instead (their
+// scores are masked, so p = 0 meets a finite value), so canary memory never
+// enters the arithmetic (a dropped block inside the cache gives unspecified
+// but in-bounds results).  A row with no key writes 0.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pda_kernels.h"
+
+namespace pda {
+namespace {
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr int kD = 256;           // head dim
+constexpr int kRows = 128;        // query rows per workgroup
+constexpr int kWaves = 8;         // 16 query rows each
+constexpr int kKT = 32;           // keys per staged tile
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileElems = kKT * kD;          // one K (or V) tile: 16 KiB
+constexpr int kChunksPerThread = kKT * (kD / 8) / kThreads;   // 16-byte pieces
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2_t v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Max / sum over the four 16-lane groups (lanes c, c + 16, c + 32, c + 48);
+// every lane of the set gets identical bits.
+__device__ __forceinline__ float group_max(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// K tile: row r's 16-byte piece j (dims 8j .. 8j + 7) sits at piece j ^ (r & 15),
+// so the 16 rows one A-operand read touches land in 16 distinct bank groups.
+__device__ __forceinline__ int kpiece(int row, int piece) {
+    return row * kD + ((piece ^ (row & 15)) << 3);
+}
+// V tile (per 16-row key block): 8-byte chunks XOR-swizzled by 4 * (row & 7),
+// so the transposed reads are free of bank conflicts.
+__device__ __forceinline__ int vchunk(int row, int chunk) {
+    return row * kD + ((chunk ^ ((row & 7) << 2)) << 2);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParams p) {
+    extern __shared__ __align__(16) uint16_t smem[];   // 2 x (K tile, V tile)
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, c = lane & 15;
+    const int h = blockIdx.x;
+    const int kvh = h / (p.nq / p.nkv);
+    // row tiles are taken last (longest causal range) first
+    const int n_tiles_q = (p.q_len + kRows - 1) / kRows;
+    const int r0 = (n_tiles_q - 1 - (int)blockIdx.y) * kRows;
+    const int row_end = min(r0 + kRows, p.q_len);
+    // keys this workgroup needs: up to its last row's position
+    const int n_keys = min(p.kv_len, p.q_offset + row_end);
+    const int n_tiles = (n_keys + kKT - 1) / kKT;
+
+    const int wr0 = r0 + wave * 16;                 // this wave's first row
+    const int qrow = min(wr0 + c, p.q_len - 1);     // the query row of lane c
+    const int qpos = p.q_offset + wr0 + c;          // its position
+    const int wave_last_pos = p.q_offset + wr0 + 15;
+    const int64_t row_s = (int64_t)p.nq * kD;       // elements between query rows
+
+    // Q as the B operand: lane = query c, 8 dims 32 kb + 8 g of k-step kb
+    bf16x8_t qb[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+        qb[kb] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(p.q + qrow * row_s + (int64_t)h * kD +
+                                                        kb * 32 + g * 8));
+
+    f32x4_t O[16];   // O[query 4g + r][dim 16 nb + c]
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = kNegInf, l = 0.f;   // of query c (same in all four groups)
+
+    // staging: thread t moves 16-byte pieces t + kThreads * i of the tile
+    // (row = idx / 32, piece = idx % 32) for K and for V
+    const uint16_t* kbase = p.k + (int64_t)kvh * kD;
+    const uint16_t* vbase = p.v + (int64_t)kvh * kD;
+    u32x4_t sk[kChunksPerThread], sv[kChunksPerThread];
+    auto stage_load = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < kChunksPerThread; ++i) {
+            const int idx = tid + kThreads * i;
+            const int row = idx >> 5, piece = idx & 31;
+            int j = tile * kKT + row;
+            int blk = j < p.kv_len ? p.table[j / p.bs] : -1;
+            if ((uint32_t)blk >= p.num_blocks) {   // past the cache or dropped: key 0
+                j = 0;
+                blk = p.table[0];
+                if ((uint32_t)blk >= p.num_blocks) blk = 0;   // (any in-pool block)
+            }
+            const int64_t off = (int64_t)blk * p.blk_s + (int64_t)(j % p.bs) * p.tok_s + piece * 8;
+            sk[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
+            sv[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+        }
+    };
+    auto stage_store = [&](int buf) {
+        uint16_t* kt = smem + buf * 2 * kTileElems;
+        uint16_t* vt = kt + kTileElems;
+#pragma unroll
+        for (int i = 0; i < kChunksPerThread; ++i) {
+            const int idx = tid + kThreads * i;
+            const int row = idx >> 5, piece = idx & 31;
+            *reinterpret_cast<u32x4_t*>(kt + kpiece(row, piece)) = sk[i];
+            *reinterpret_cast<u32x4_t*>(vt + (row >> 4) * 16 * kD + vchunk(row & 15, 2 * piece)) =
+                sv[i];
+        }
+    };
+
+    if (n_tiles > 0) {
+        stage_load(0);
+        stage_store(0);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < n_tiles; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < n_tiles) stage_load(t + 1);
+        const uint16_t* kt = smem + buf * 2 * kTileElems;
+        const uint16_t* vt = kt + kTileElems;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const int key0 = t * kKT + kb2 * 16;
+            if (key0 > wave_last_pos || key0 >= p.kv_len) continue;   // wave-uniform
+            // S^T = K . Q^T over the 256 dims
+            const int krow = kb2 * 16 + c;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+                const bf16x8_t ka = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + kpiece(krow, 4 * kb + g)));
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kb], acc, 0, 0, 0);
+            }
+            // acc[r]: key key0 + 4g + r, query c
+            float s[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = key0 + 4 * g + r;
+                s[r] = key <= qpos && key < p.kv_len ? acc[r] * p.c : kNegInf;
+            }
+            const float tmax = group_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+            const float mn = fmaxf(m, tmax);
+            const float ms = mn == kNegInf ? 0.f : mn;
+            const float alpha = fexp2(m - ms);
+            const bool grow = mn != m;
+            m = mn;
+            float pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pr[r] = fexp2(s[r] - ms);
+            l = l * alpha + group_sum((pr[0] + pr[1]) + (pr[2] + pr[3]));
+            // P as the A operand: lane = query c, keys 4g .. 4g + 3 (in place)
+            const s16x4_t pa = __builtin_bit_cast(
+                s16x4_t,
+                uint64_t(pack_bf16x2(pr[0], pr[1])) | (uint64_t(pack_bf16x2(pr[2], pr[3])) << 32));
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                // O rows are queries 4g + r; their factor lives in lane 4g + r
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float a = __int_as_float(
+                        __builtin_amdgcn_ds_bpermute((4 * g + r) * 4, __float_as_int(alpha)));
+#pragma unroll
+                    for (int nb = 0; nb < 16; ++nb) O[nb][r] *= a;
+                }
+            }
+            // O += P . V; V^T read transposed: lane c of group g addresses
+            // row 4g + c/4, chunk 4 nb + c%4 of this key block
+            const uint16_t* vkb = vt + kb2 * 16 * kD;
+            const int trow = 4 * g + (c >> 2);
+#pragma unroll
+            for (int nb = 0; nb < 16; ++nb) {
+                typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_p;
+                const uint16_t* src = vkb + vchunk(trow, 4 * nb + (c & 3));
+                const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_p)(__attribute__((address_space(3))) uint16_t*)src);
+                O[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nb], 0, 0, 0);
+            }
+        }
+        if (t + 1 < n_tiles) stage_store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // out = O / l (0 where l is 0), rows 4g + r of this wave
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float L =
+            __int_as_float(__builtin_amdgcn_ds_bpermute((4 * g + r) * 4, __float_as_int(l)));
+        const int row = wr0 + 4 * g + r;
+        if (row >= p.q_len) continue;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        uint16_t* dst = p.out + row * row_s + (int64_t)h * kD + c;
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) {
+            const __bf16 b = (__bf16)(L > 0.f ? O[nb][r] * inv : 0.f);
+            dst[nb * 16] = __builtin_bit_cast(uint16_t, b);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+    const size_t lds = sizeof(uint16_t) * 4 * (size_t)kTileElems;   // 64 KiB
+    const dim3 grid((uint32_t)p.nq, (uint32_t)((p.q_len + kRows - 1) / kRows));
+    hipLaunchKernelGGL(prefill_kernel, grid, dim3(kThreads), lds, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace pda

@@ -185,3 +185,31 @@ def test_plan_tiles_covers_every_token_once_in_order(bs, cap):
             toks += [(blk, k) for k in range(nvalid)]
         expect = [(tables[s][t // bs], t % bs) for t in range(L)]
         assert toks == expect, s
+
+
+def test_prefill_gate_and_validation():
+    assert P.pda_prefill_applies(32, 4, 256)
+    assert not P.pda_prefill_applies(32, 4, 128)
+    assert not P.pda_prefill_applies(32, 4, 256, causal=False)
+    assert not P.pda_prefill_applies(32, 4, 256, sliding_window=512)
+    assert not P.pda_prefill_applies(30, 4, 256)
+    assert not P.pda_prefill_applies(32, 0, 256)
+
+    def pf(**kw):
+        a = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, out=FAKE, block_table=FAKE, q_len=16,
+                 kv_len=16, q_offset=0, num_q_heads=8, num_kv_heads=2, head_dim=256,
+                 block_size=16, max_blocks=1, num_blocks=1, scale=0.0625, sliding_window=0,
+                 stream=0)
+        a.update(kw)
+        return P.pda_paged_prefill(**a)
+
+    # not applicable: nothing is checked further, nothing launched
+    assert pf(q_len=0) == P.PDA_NOT_APPLICABLE
+    assert pf(head_dim=128) == P.PDA_NOT_APPLICABLE
+    assert pf(sliding_window=8) == P.PDA_NOT_APPLICABLE
+    assert pf(num_q_heads=7) == P.PDA_NOT_APPLICABLE
+    for bad in (dict(q=0), dict(block_table=0), dict(block_size=0), dict(num_blocks=0),
+                dict(kv_len=17), dict(q_offset=2**31 - 8), dict(scale=float("nan"))):
+        with pytest.raises(P.PdaError) as e:
+            pf(**bad)
+        assert e.value.code == P.PDA_EINVAL
