@@ -13,10 +13,12 @@
 //   online softmax (FP32, base 2) on the accumulator: each query's 16
 //       scores sit in one column across the four 16-lane groups; the causal
 //       mask and the end of the cache turn scores into -inf there.
-//   O[16 query][256] += P[16][16] . V[16][256]
-//       16 x v_mfma_f32_16x16x16_bf16; the S^T accumulator is P in the
-//       A-operand layout, V comes back from LDS transposed by
-//       ds_read_b64_tr_b16.
+//   O[16 query][256] += P[16][32] . V[32][256] per 32-key tile
+//       16 x v_mfma_f32_16x16x32_bf16; the two S^T accumulators of the tile
+//       are P in the A-operand layout (lane = query, k index 8g + t = key
+//       4g + t of the first block or 4g + t - 4 of the second), and the B
+//       operand takes V in the same k order from two ds_read_b64_tr_b16
+//       transposed reads of the LDS tile.
 //
 // Query row i is the token at position q_offset + i and attends the keys at
 // positions j <= q_offset + i with j < kv_len.  K / V rows past kv_len, or in
@@ -34,9 +36,15 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kD = 256;           // head dim
-constexpr int kRows = 128;        // query rows per workgroup
-constexpr int kWaves = 8;         // 16 query rows each
-constexpr int kKT = 32;           // keys per staged tile
+#ifndef PDA_PREFILL_WAVES
+#define PDA_PREFILL_WAVES 8
+#endif
+constexpr int kWaves = PDA_PREFILL_WAVES;   // 16 query rows each
+constexpr int kRows = 16 * kWaves;          // query rows per workgroup
+constexpr int kKT = 32;           // keys per staged tile (two 16-key blocks)
+#ifndef PDA_PREFILL_XCD
+#define PDA_PREFILL_XCD 1
+#endif
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileElems = kKT * kD;          // one K (or V) tile: 16 KiB
 constexpr int kChunksPerThread = kKT * (kD / 8) / kThreads;   // 16-byte pieces
@@ -88,7 +96,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;
-    const int h = blockIdx.x;
+    // Workgroup ids go to the 8 XCDs round-robin (id % 8).  When the head
+    // count is a multiple of 8, XCD x takes the consecutive heads
+    // x * nq/8 .. x * nq/8 + nq/8 - 1, which share KV heads, so each XCD's
+    // L2 holds the K/V of one or two KV heads instead of all of them.  Only
+    // the placement changes.
+    const int h = PDA_PREFILL_XCD && p.nq % 8 == 0
+                      ? ((int)blockIdx.x % 8) * (p.nq / 8) + (int)blockIdx.x / 8
+                      : (int)blockIdx.x;
     const int kvh = h / (p.nq / p.nkv);
     // row tiles are taken last (longest causal range) first
     const int n_tiles_q = (p.q_len + kRows - 1) / kRows;
@@ -163,40 +178,53 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
         if (t + 1 < n_tiles) stage_load(t + 1);
         const uint16_t* kt = smem + buf * 2 * kTileElems;
         const uint16_t* vt = kt + kTileElems;
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            const int key0 = t * kKT + kb2 * 16;
-            if (key0 > wave_last_pos || key0 >= p.kv_len) continue;   // wave-uniform
-            // S^T = K . Q^T over the 256 dims
-            const int krow = kb2 * 16 + c;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        const int key0 = t * kKT;
+        // wave-uniform: the tile (or its second 16-key block) lies past every
+        // row of this wave, or past the cache
+        if (key0 <= wave_last_pos && key0 < p.kv_len) {
+            const bool live1 = key0 + 16 <= wave_last_pos && key0 + 16 < p.kv_len;
+            // S^T = K . Q^T over the 256 dims, both 16-key blocks interleaved
+            f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) {
-                const bf16x8_t ka = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + kpiece(krow, 4 * kb + g)));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kb], acc, 0, 0, 0);
+                const bf16x8_t ka0 = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + kpiece(c, 4 * kb + g)));
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qb[kb], acc0, 0, 0, 0);
+                if (live1) {
+                    const bf16x8_t ka1 = __builtin_bit_cast(
+                        bf16x8_t,
+                        *reinterpret_cast<const u32x4_t*>(kt + kpiece(16 + c, 4 * kb + g)));
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qb[kb], acc1, 0, 0, 0);
+                }
             }
-            // acc[r]: key key0 + 4g + r, query c
-            float s[4];
+            // one softmax step over the tile's 32 keys; acc_b[r]: key
+            // key0 + 16 b + 4g + r, query c
+            float s[8];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = key0 + 4 * g + r;
-                s[r] = key <= qpos && key < p.kv_len ? acc[r] * p.c : kNegInf;
+                const int k0 = key0 + 4 * g + r, k1 = k0 + 16;
+                s[r] = k0 <= qpos && k0 < p.kv_len ? acc0[r] * p.c : kNegInf;
+                s[4 + r] = live1 && k1 <= qpos && k1 < p.kv_len ? acc1[r] * p.c : kNegInf;
             }
-            const float tmax = group_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+            float lmax = s[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) lmax = fmaxf(lmax, s[i]);
+            const float tmax = group_max(lmax);
             const float mn = fmaxf(m, tmax);
             const float ms = mn == kNegInf ? 0.f : mn;
             const float alpha = fexp2(m - ms);
             const bool grow = mn != m;
             m = mn;
-            float pr[4];
+            float pr[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pr[r] = fexp2(s[r] - ms);
-            l = l * alpha + group_sum((pr[0] + pr[1]) + (pr[2] + pr[3]));
-            // P as the A operand: lane = query c, keys 4g .. 4g + 3 (in place)
-            const s16x4_t pa = __builtin_bit_cast(
-                s16x4_t,
-                uint64_t(pack_bf16x2(pr[0], pr[1])) | (uint64_t(pack_bf16x2(pr[2], pr[3])) << 32));
+            for (int i = 0; i < 8; ++i) pr[i] = fexp2(s[i] - ms);
+            l = l * alpha +
+                group_sum(((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+            // P as the A operand of a 32-key step: lane = query c, k index
+            // 8g + t = key 4g + t of block 0 (t < 4) or of block 1 (t >= 4)
+            const u32x4_t pw = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+            const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pw);
             if (__builtin_amdgcn_ballot_w64(grow) != 0) {
                 // O rows are queries 4g + r; their factor lives in lane 4g + r
 #pragma unroll
@@ -207,17 +235,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
                     for (int nb = 0; nb < 16; ++nb) O[nb][r] *= a;
                 }
             }
-            // O += P . V; V^T read transposed: lane c of group g addresses
-            // row 4g + c/4, chunk 4 nb + c%4 of this key block
-            const uint16_t* vkb = vt + kb2 * 16 * kD;
+            // O += P . V with the same k order on the B side: the transposed
+            // reads of the two blocks (lane c of group g addresses row
+            // 4g + c/4, chunk 4 nb + c%4) give keys 4g .. 4g + 3 of each
             const int trow = 4 * g + (c >> 2);
 #pragma unroll
             for (int nb = 0; nb < 16; ++nb) {
                 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_p;
-                const uint16_t* src = vkb + vchunk(trow, 4 * nb + (c & 3));
-                const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_p)(__attribute__((address_space(3))) uint16_t*)src);
-                O[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nb], 0, 0, 0);
+                const uint16_t* src0 = vt + vchunk(trow, 4 * nb + (c & 3));
+                const uint16_t* src1 = src0 + 16 * kD;
+                const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_p)(__attribute__((address_space(3))) uint16_t*)src0);
+                const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_p)(__attribute__((address_space(3))) uint16_t*)src1);
+                const bf16x8_t vb =
+                    __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, O[nb], 0, 0, 0);
             }
         }
         if (t + 1 < n_tiles) stage_store(buf ^ 1);
@@ -244,7 +277,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-    const size_t lds = sizeof(uint16_t) * 4 * (size_t)kTileElems;   // 64 KiB
+    const size_t lds = sizeof(uint16_t) * 4 * (size_t)kTileElems;   // 2 x (K, V) tiles
+    if (lds > 64 * 1024) {
+        static bool granted = false;   // racy first calls only repeat the request
+        if (!granted) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds);
+            if (e != hipSuccess) return e;
+            granted = true;
+        }
+    }
     const dim3 grid((uint32_t)p.nq, (uint32_t)((p.q_len + kRows - 1) / kRows));
     hipLaunchKernelGGL(prefill_kernel, grid, dim3(kThreads), lds, stream, p);
     return hipGetLastError();
