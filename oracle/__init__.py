@@ -15,6 +15,8 @@ Contents
 ``oracle.geometry``   the launch-geometry formulas of the attn_splitk module
                       page, written out in Python integers.
 ``oracle.prefill``    causal paged prefill (the prefill page's kernel), FP64.
+``oracle.fp8``        paged decode over an FP8 (OCP E4M3) cache with per-tensor
+                      scales, FP64 (scale semantics: parity unpinned).
 ``oracle.policy``     that page's policy grammar and resolution rules
                       (parse, parse_gqa_pack, resolve_policy,
                       resolve_gqa_pack).
@@ -26,7 +28,8 @@ tokens, q = 0, equal keys, empty sequence), invariances (block-table
 permutation with a matching pool relayout, merge of per-split partials), and
 the worked numbers printed on the attn_splitk module page.
 
-Parity unpinned: the split partition rule (``geometry.split_chunk``) and the
+Parity unpinned: the FP8 scale semantics (``oracle.fp8``; the pages name FP8
+launches but print no format or scaling), the split partition rule (``geometry.split_chunk``) and the
 value of the per-split floor, and the reading of the tiled call's
 ``last_block_valid_slots``, have no value printed on the pages; they are
 checked only for self-consistency (partials merge to the one-pass result;

@@ -47,6 +47,36 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return out
 
 
+E4M3_QNAN = np.uint8(0x7F)
+
+
+def _e4m3_magnitudes() -> np.ndarray:
+    """The 127 non-negative finite values of the OCP FP8 E4M3 ("fn") format,
+    indexed by their 7-bit code (sign clear): exponent bias 7, 3 mantissa bits,
+    subnormals at exponent field 0, code 0x7F reserved for NaN."""
+    codes = np.arange(127)
+    e, m = codes >> 3, codes & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7))
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round values to OCP FP8 E4M3 (nearest, ties to the even code), with
+    magnitudes past the largest finite value (448) saturating to it; NaN
+    becomes the NaN code.  An input-generation helper (quantising synthetic
+    data); it decodes nothing for either side."""
+    x = np.asarray(x, dtype=np.float64)
+    mags = _e4m3_magnitudes()
+    a = np.minimum(np.abs(x), mags[-1])
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - mags[lo], mags[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code |= np.where(np.signbit(x), np.uint8(0x80), np.uint8(0))
+    code[np.isnan(x)] = E4M3_QNAN
+    return code
+
+
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Widen BF16 bit patterns to FP32 (exact).  A convenience for callers
     that want to look at generated data; the oracle decodes on its own."""
@@ -389,3 +419,85 @@ def make_prefill(w: Workload | str, canary: bool = True, q_len: int | None = Non
         v_cache[tables[0, :n]] = v
     scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
     return PrefillInputs(w, q, k_cache, v_cache, tables[0].copy(), kv, qo, scale)
+
+
+@dataclasses.dataclass
+class PagedFP8Inputs:
+    """A paged-decode batch with an FP8 (OCP E4M3) KV cache and per-tensor
+    FP32 scales: K = decode(k8) * k_scale, V = decode(v8) * v_scale.
+
+    q            uint16 [num_seqs, num_q_heads, head_dim]   (BF16 bits)
+    k8, v8       uint8  [num_blocks, block_size, num_kv_heads, head_dim]
+    block_tables int32  [num_seqs, max_blocks_per_seq]  (-1 = unused)
+    seq_lens     int32  [num_seqs]
+    """
+    workload: Workload
+    q: np.ndarray
+    k8: np.ndarray
+    v8: np.ndarray
+    block_tables: np.ndarray
+    seq_lens: np.ndarray
+    scale: float
+    k_scale: float
+    v_scale: float
+
+    @property
+    def num_seqs(self): return self.q.shape[0]
+    @property
+    def num_q_heads(self): return self.q.shape[1]
+    @property
+    def head_dim(self): return self.q.shape[2]
+    @property
+    def num_kv_heads(self): return self.k8.shape[2]
+    @property
+    def block_size(self): return self.k8.shape[1]
+    @property
+    def num_blocks(self): return self.k8.shape[0]
+
+
+def make_paged_fp8(w: Workload | str, canary: bool = True, seq_lens=None,
+                   k_scale: float | None = None, v_scale: float | None = None) -> PagedFP8Inputs:
+    """The paged recipe above with the K / V draws (FP32 N(0, 1), step 5)
+    quantised to E4M3 instead of BF16: each tensor is divided by its scale
+    and rounded (``f32_to_e4m3_bits``).  The scales default to a fixed
+    ``4.0 / 448`` (so |x| up to 4 is representable, larger values saturate);
+    they are FP32 values.  Canaries are the E4M3 NaN code."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    assert w.layout == "paged"
+    rng = np.random.default_rng(w.seed)
+    lens = _draw_lens(w, rng)
+    if seq_lens is not None:
+        lens = np.asarray(seq_lens, dtype=np.int64)
+        w = dataclasses.replace(w, num_seqs=len(lens), seq_lens=tuple(int(x) for x in lens),
+                                len_range=None, forced=())
+    bs, nkv, D, nq = w.block_size, w.num_kv_heads, w.head_dim, w.num_q_heads
+    nblk, pool_blocks, tables = _layout(w, rng, lens, bs)
+    q = f32_to_bf16_bits(rng.standard_normal((len(lens), nq, D), dtype=np.float32))
+    ks = float(np.float32(4.0 / 448.0 if k_scale is None else k_scale))
+    vs = float(np.float32(4.0 / 448.0 if v_scale is None else v_scale))
+    fill = E4M3_QNAN if canary else np.uint8(0)
+    k8 = np.full((max(pool_blocks, 1), bs, nkv, D), fill, dtype=np.uint8)
+    v8 = np.full((max(pool_blocks, 1), bs, nkv, D), fill, dtype=np.uint8)
+
+    def one(s):
+        n = int(nblk[s])
+        if n == 0:
+            return
+        r = np.random.default_rng([w.seed, s])
+        k = r.standard_normal((n, bs, nkv, D), dtype=np.float32)
+        v = r.standard_normal((n, bs, nkv, D), dtype=np.float32)
+        kq = f32_to_e4m3_bits(k.astype(np.float64) / ks)
+        vq = f32_to_e4m3_bits(v.astype(np.float64) / vs)
+        tail = int(lens[s]) - (n - 1) * bs
+        if canary and tail < bs:
+            kq[n - 1, tail:] = E4M3_QNAN
+            vq[n - 1, tail:] = E4M3_QNAN
+        ids = tables[s, :n]
+        k8[ids] = kq
+        v8[ids] = vq
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, range(len(lens))))
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    return PagedFP8Inputs(w, q, k8, v8, tables, lens.astype(np.int32), scale, ks, vs)
