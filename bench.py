@@ -35,10 +35,11 @@ FOLD_SRC = os.path.join(ROOT, "paged_decode_attention_splitk_amd", "csrc", "deco
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fold_batch_traffic.json")
 
 
-def alg_bytes(inp, n_splits):
+def alg_bytes(inp, n_splits, kv_elem=2):
     """Algorithmic HBM bytes of one decode step and of its two kernels.
 
-    fold:  K and V of every valid token (num_kv_heads * head_dim * 2 B each),
+    fold:  K and V of every valid token (num_kv_heads * head_dim * kv_elem B
+           each: 2 for BF16, 1 for an E4M3 cache),
            q, the block-table entries and lengths read, the workspace written;
     merge: the workspace read, the BF16 output written.
     """
@@ -46,7 +47,7 @@ def alg_bytes(inp, n_splits):
     lens = inp.seq_lens.astype(np.int64)
     S, nq, D = inp.q.shape
     nkv, bs = inp.num_kv_heads, inp.block_size
-    kv = int(lens.sum()) * nkv * D * 2 * 2
+    kv = int(lens.sum()) * nkv * D * kv_elem * 2
     q = S * nq * D * 2
     tables = int(((lens + bs - 1) // bs).sum()) * 4 + S * 4
     ws = S * nq * n_splits * (D + 2) * 4 if n_splits > 1 else 0
@@ -72,17 +73,22 @@ def load_traffic(per_launch_alg):
     return rec.get("fold_hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, seconds):
+def cpu_baseline(inp, seconds, fp8=False):
     """The FP64 oracle on the host, one BLAS thread, repeated over the whole
     batch until `seconds` have passed (at least once)."""
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as A
+    from oracle import fp8 as F
     reps, t0 = 0, time.perf_counter()
     with threadpool_limits(1):
         while True:
-            A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
-                           inp.scale)
+            if fp8:
+                F.paged_decode_fp8(inp.q, inp.k8, inp.v8, inp.block_tables, inp.seq_lens,
+                                   inp.scale, inp.k_scale, inp.v_scale)
+            else:
+                A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                               inp.seq_lens, inp.scale)
             reps += 1
             el = time.perf_counter() - t0
             if el >= seconds:
@@ -147,7 +153,7 @@ def tiled_bench(args, K):
     # algorithmic bytes: valid K/V once; per active (call, sequence) its q,
     # its tile-table entries and a read + write of its (m, l, o) state; the
     # fill pass writes the state, finalize reads l, o and writes out
-    kv = int(lens.sum()) * nkv * D * 2 * 2
+    kv = int(lens.sum()) * nkv * D * kv_elem * 2
     state_slot = nq * (D + 2) * 4
     tiles_b = kv
     for tb, cnt, lbvs in calls:
@@ -248,6 +254,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="KV pool copies (default: >= 1 GB)")
     ap.add_argument("--packed", action="store_true",
                     help="run the GQA-packed MFMA kernel (single split; packed workload shape)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 (E4M3) KV cache of the same shape (pda_*_fp8 entry points)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -276,7 +284,11 @@ def main():
         print(json.dumps(rec), flush=True)
         return
 
-    inp = W.make_paged(args.workload, canary=False)
+    if args.fp8 and args.packed:
+        sys.exit("--fp8 has no packed kernel")
+    inp = (W.make_paged_fp8(args.workload, canary=False) if args.fp8 else
+           W.make_paged(args.workload, canary=False))
+    k_host, v_host = (inp.k8, inp.v8) if args.fp8 else (inp.k_cache, inp.v_cache)
     S, nq, D = inp.q.shape
     nkv, bs = inp.num_kv_heads, inp.block_size
     n = args.splits or P.pda_num_splits(P.PDA_SPLITK_AUTO, 0, CU_COUNT, nq, S, 0)
@@ -284,17 +296,18 @@ def main():
         if not P.pda_gqa_pack_shape_ok(nq, nkv, D):
             sys.exit(f"--packed needs 8 q heads per kv head at head_dim 256 (got {nq}/{nkv}/{D})")
         n = args.splits or 1   # the packed kernels' own (non-split) launch unless pinned
-    ab = alg_bytes(inp, n)
+    ab = alg_bytes(inp, n, 1 if args.fp8 else 2)
     copies = args.copies or max(1, math.ceil(1.0e9 / ab["kv"]))
 
     def up(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a if a.dtype == np.uint8 else a.view(np.int16)).cuda()
 
     q = up(inp.q)
     bt = torch.from_numpy(inp.block_tables).cuda()
     lens = torch.from_numpy(inp.seq_lens).cuda()
-    ks = [up(inp.k_cache) for _ in range(copies)]
-    vs = [up(inp.v_cache) for _ in range(copies)]
+    ks = [up(k_host) for _ in range(copies)]
+    vs = [up(v_host) for _ in range(copies)]
     wsf = P.pda_workspace_slots(S, nq, n, D)
     ws = torch.empty(max(wsf, 1), dtype=torch.float32, device="cuda")
     out = torch.empty((S, nq, D), dtype=torch.int16, device="cuda")
@@ -305,7 +318,17 @@ def main():
     flags = P.PDA_DECODE_PACKED if args.packed else P.PDA_DECODE_UNPACKED
 
     def partials(i):
-        if n == 1:
+        if args.fp8:
+            if n == 1:
+                rc = P.pda_paged_decode_fp8(q, ks[i % copies], vs[i % copies], bt, lens, out,
+                                            None, 0, S, nq, nkv, D, bs, mb, inp.num_blocks,
+                                            inp.scale, inp.k_scale, inp.v_scale, 1, flags, sp)
+                assert rc == P.PDA_OK
+            else:
+                P.pda_splitk_partials_fp8(q, ks[i % copies], vs[i % copies], bt, lens, ws, wsf,
+                                          S, nq, nkv, D, bs, mb, inp.num_blocks, inp.scale,
+                                          inp.k_scale, inp.v_scale, n, sp)
+        elif n == 1:
             rc = P.pda_paged_decode(q, ks[i % copies], vs[i % copies], bt, lens, out, None, 0, S,
                                     nq, nkv, D, bs, mb, inp.num_blocks, inp.scale, 1, flags, sp)
             assert rc == P.PDA_OK
@@ -361,7 +384,8 @@ def main():
 
     value = ab["step"] / (ms_per_step * 1e-3) / 1e9
     achieved = ab["fold"] / (fold_avg * 1e-3) / 1e9
-    traffic = None if (args.packed or args.workload != "batch") else load_traffic(ab["fold"])
+    traffic = (None if (args.packed or args.fp8 or args.workload != "batch")
+               else load_traffic(ab["fold"]))
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -373,7 +397,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8e4m3 kv, bf16 q/out" if args.fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": inp.workload.description,
@@ -382,6 +406,7 @@ def main():
             "seq_len_min": int(inp.seq_lens.min()), "seq_len_max": int(inp.seq_lens.max()),
             "num_splits": n, "policy_cu_count": CU_COUNT, "device_cu_count": dev_cus,
             "kv_pool_copies": copies, "algorithmic_bytes_per_step": ab["step"],
+            "kv_cache": "fp8 e4m3, per-tensor scales" if args.fp8 else "bf16",
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -392,7 +417,8 @@ def main():
         "roofline": {
             "kernel": (f"GQA-packed MFMA decode (packed_kernel<{'true' if n > 1 else 'false'}>)"
                        if args.packed else
-                       f"split-K fold (fold_kernel<{0 if n > 1 else 1},{D},{min(nq // nkv, 8)}>)"),
+                       f"split-K fold (fold_kernel<{0 if n > 1 else 1},{D},{min(nq // nkv, 8)},"
+                       f"{'true' if args.fp8 else 'false'}>)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -410,7 +436,7 @@ def main():
         rec["mfma"] = {"tflops": round(tflops, 2), "peak_bf16_tflops": 2500.0,
                        "utilisation": round(tflops / 2500.0, 5)}
     if not args.no_cpu:
-        sec, reps = cpu_baseline(inp, args.cpu_seconds)
+        sec, reps = cpu_baseline(inp, args.cpu_seconds, args.fp8)
         rec["cpu_baseline"] = {
             "value": round(ab["step"] / sec / 1e9, 4),
             "unit": "GB/s",

@@ -126,6 +126,42 @@ uint64_t pda_gqa_pack_ctas(uint32_t num_kv_heads, uint32_t num_seqs);
 uint32_t pda_split_chunk(uint32_t seq_len, uint32_t num_splits, uint32_t block_size);
 
 /* ------------------------------------------------------------------------
+ * One-shot paged decode over an FP8 KV cache (attn_splitk page: the FP8
+ * paged-decode launches it names; the format and scaling are this
+ * library's reading, as the page prints neither).
+ *
+ * Same as pda_paged_decode except:
+ *   k_cache, v_cache  uint8 [num_blocks, block_size, num_kv_heads, head_dim],
+ *                     OCP FP8 E4M3 codes (bias 7, 3 mantissa bits,
+ *                     subnormals, S.1111.111 = NaN, largest finite 448)
+ *   k_scale, v_scale  per-tensor FP32 scales: K = decode(k) * k_scale,
+ *                     V = decode(v) * v_scale (scores are
+ *                     scale * q . K; the workspace partials hold o of the
+ *                     scaled V)
+ *   flags             PDA_DECODE_UNPACKED or PDA_DECODE_DEFAULT; there is no
+ *                     packed FP8 kernel (PDA_DECODE_PACKED: NOT_APPLICABLE)
+ * q stays BF16 and out is BF16; the caches need 8-byte alignment (16 is what
+ * pda_paged_decode asks and is checked the same way).
+ * ------------------------------------------------------------------------ */
+int pda_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                         float* workspace, uint64_t workspace_floats, uint32_t num_seqs,
+                         uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                         uint32_t block_size, uint32_t max_blocks_per_seq, uint32_t num_blocks,
+                         float scale, float k_scale, float v_scale, uint32_t num_splits,
+                         uint32_t flags, void* stream);
+
+/* pda_paged_decode_fp8 without the merge (num_splits >= 2): leaves the
+ * partials in the workspace; pda_splitk_merge finishes them. */
+int pda_splitk_partials_fp8(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            float* workspace, uint64_t workspace_floats, uint32_t num_seqs,
+                            uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                            uint32_t block_size, uint32_t max_blocks_per_seq,
+                            uint32_t num_blocks, float scale, float k_scale, float v_scale,
+                            uint32_t num_splits, void* stream);
+
+/* ------------------------------------------------------------------------
  * Causal paged prefill (prefill page "prefill_attn_fa128.rs": `applies` and
  * the `paged` launcher; head dim 256, 128 query rows per workgroup).
  * ------------------------------------------------------------------------ */

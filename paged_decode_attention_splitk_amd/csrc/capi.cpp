@@ -186,9 +186,12 @@ pda::PackedParams packed_params(const DecodeShape& s, const void* q, const void*
     return p;
 }
 
+// kv8: the caches hold OCP E4M3 bytes with per-tensor scales k_scale / v_scale
+// (the fold kernel's FP8 form; never packed).
 int run_partials(const DecodeShape& s, const void* q, const void* k, const void* v,
                  const int32_t* bt, const int32_t* lens, float* ws, uint64_t ws_floats,
-                 float scale, uint32_t nsplit, bool packed, hipStream_t stream) {
+                 float scale, uint32_t nsplit, bool packed, hipStream_t stream,
+                 bool kv8 = false, float k_scale = 1.f, float v_scale = 1.f) {
     if (!ws) return fail(PDA_EINVAL, "workspace is NULL with num_splits > 1");
     if (!aligned(ws, 8)) return fail(PDA_EINVAL, "workspace must be 8-byte aligned");
     const uint64_t need = pda_workspace_slots(s.num_seqs, s.nq, nsplit, s.D);
@@ -204,12 +207,14 @@ int run_partials(const DecodeShape& s, const void* q, const void* k, const void*
     }
     int hg = 0;
     const int gc = head_groups(s.nq / s.nkv, &hg);
-    pda::FoldParams p = fold_params(s, q, k, v, bt, lens, hg, scale, nsplit);
+    pda::FoldParams p = fold_params(s, q, k, v, bt, lens, hg, kv8 ? scale * k_scale : scale,
+                                    nsplit);
     p.ws = ws;
+    p.v_scale = v_scale;
     const int waves = oneshot_waves(s.nkv, nsplit, s.D, gc);
     const uint64_t gx = (uint64_t)s.nkv * hg * nsplit;
     hipError_t e = pda::launch_fold(pda::kModePartial, (int)s.D, gc, p, (uint32_t)gx, s.num_seqs,
-                                    waves, stream);
+                                    waves, stream, kv8);
     if (e != hipSuccess) return hip_fail(e, "split-K partial launch");
     return PDA_OK;
 }
@@ -253,6 +258,72 @@ int pda_splitk_partials(const void* q, const void* k_cache, const void* v_cache,
     if (num_seqs == 0) return ok();
     rc = run_partials(s, q, k_cache, v_cache, block_tables, seq_lens, workspace, workspace_floats,
                       scale, num_splits, packed, (hipStream_t)stream);
+    return rc == PDA_OK ? ok() : rc;
+}
+
+int pda_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                         float* workspace, uint64_t workspace_floats, uint32_t num_seqs,
+                         uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                         uint32_t block_size, uint32_t max_blocks_per_seq, uint32_t num_blocks,
+                         float scale, float k_scale, float v_scale, uint32_t num_splits,
+                         uint32_t flags, void* stream) {
+    const DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, max_blocks_per_seq, num_blocks};
+    int rc = check_decode(s, q, k_cache, v_cache, block_tables, seq_lens, out, true);
+    if (rc != PDA_OK) return rc;
+    if (flags > PDA_DECODE_DEFAULT) return fail(PDA_EINVAL, "unknown flags 0x%x", flags);
+    if (num_splits < 1 || num_splits > pda::kMaxDecodeSplits)
+        return fail(PDA_EINVAL, "num_splits %u outside 1..%u", num_splits, pda::kMaxDecodeSplits);
+    if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+        return fail(PDA_EINVAL, "scale, k_scale and v_scale must be finite");
+    if (flags == PDA_DECODE_PACKED) {
+        g_last_error = "no packed kernel for an FP8 cache";
+        return PDA_NOT_APPLICABLE;
+    }
+    if (num_seqs == 0) return ok();
+    hipStream_t st = (hipStream_t)stream;
+    if (num_splits == 1) {
+        int hg = 0;
+        const int gc = head_groups(num_q_heads / num_kv_heads, &hg);
+        pda::FoldParams p = fold_params(s, q, k_cache, v_cache, block_tables, seq_lens, hg,
+                                        scale * k_scale, 1);
+        p.out = static_cast<uint16_t*>(out);
+        p.v_scale = v_scale;
+        const int waves = oneshot_waves(num_kv_heads, 1, head_dim, gc);
+        hipError_t e = pda::launch_fold(pda::kModeFinal, (int)head_dim, gc, p,
+                                        (uint32_t)(num_kv_heads * hg), num_seqs, waves, st, true);
+        if (e != hipSuccess) return hip_fail(e, "single-split FP8 decode launch");
+        return ok();
+    }
+    rc = run_partials(s, q, k_cache, v_cache, block_tables, seq_lens, workspace, workspace_floats,
+                      scale, num_splits, false, st, true, k_scale, v_scale);
+    if (rc != PDA_OK) return rc;
+    hipError_t e = pda::launch_merge(workspace, static_cast<uint16_t*>(out), num_seqs,
+                                     (int)num_q_heads, (int)head_dim, (int)num_splits, st);
+    if (e != hipSuccess) return hip_fail(e, "split-K merge launch");
+    return ok();
+}
+
+int pda_splitk_partials_fp8(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            float* workspace, uint64_t workspace_floats, uint32_t num_seqs,
+                            uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                            uint32_t block_size, uint32_t max_blocks_per_seq,
+                            uint32_t num_blocks, float scale, float k_scale, float v_scale,
+                            uint32_t num_splits, void* stream) {
+    const DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, max_blocks_per_seq, num_blocks};
+    int rc = check_decode(s, q, k_cache, v_cache, block_tables, seq_lens, nullptr, false);
+    if (rc != PDA_OK) return rc;
+    if (num_splits < 2 || num_splits > pda::kMaxDecodeSplits)
+        return fail(PDA_EINVAL, "num_splits %u outside 2..%u for a partials launch", num_splits,
+                    pda::kMaxDecodeSplits);
+    if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+        return fail(PDA_EINVAL, "scale, k_scale and v_scale must be finite");
+    if (num_seqs == 0) return ok();
+    rc = run_partials(s, q, k_cache, v_cache, block_tables, seq_lens, workspace, workspace_floats,
+                      scale, num_splits, false, (hipStream_t)stream, true, k_scale, v_scale);
     return rc == PDA_OK ? ok() : rc;
 }
 

@@ -55,6 +55,8 @@ constexpr float kNegInf = -__builtin_inff();
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -227,7 +229,7 @@ struct FoldShape {
 // per SIMD fit their registers), 8 beyond.
 __host__ __device__ constexpr int fold_max_threads(int gc) { return gc <= 6 ? 768 : 512; }
 
-template <int MODE, int D, int GC>
+template <int MODE, int D, int GC, bool KV8>
 __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldParams p) {
     using S = FoldShape<D, GC>;
     constexpr int LPT = S::LPT, ROWS = S::ROWS, U = S::U, TG = S::TG, NP = S::NP,
@@ -312,20 +314,23 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
     float* trow = tw + row * TROW;                   // partials of this row
     float* xrow = tw + ROWS * TROW + row * XS;       // exchange record of this row
 
-    const int tok_b = (int)p.tok_s * 2;
+    // element bytes: 2 (BF16 cache) or 1 (FP8 E4M3 cache); a lane's 8 dims
+    // are one 16- or 8-byte load
+    constexpr int EB = KV8 ? 1 : 2;
+    const int tok_b = (int)p.tok_s * EB;
     uint32_t voff[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) voff[u] = (uint32_t)((row + ROWS * u) * tok_b + sub * 16);
-    const uint32_t voff0 = (uint32_t)(sub * 16);               // the group's first token
-    const uint32_t rec = (uint32_t)((p.bs - 1) * tok_b + D * 2);  // bytes a block spans
+    for (int u = 0; u < U; ++u) voff[u] = (uint32_t)((row + ROWS * u) * tok_b + sub * 8 * EB);
+    const uint32_t voff0 = (uint32_t)(sub * 8 * EB);           // the group's first token
+    const uint32_t rec = (uint32_t)((p.bs - 1) * tok_b + D * EB);  // bytes a block spans
 
     // a live range starts on a block (hence group) boundary; an empty split
     // starts at the sequence end, which need not be aligned: it folds nothing
     const int gpb = p.bs / TG;  // groups per block
     const int g_first = t_begin / TG;
     const int g_end = t_end > t_begin ? (t_end + TG - 1) / TG : g_first;
-    const uint16_t* kh = p.k + (int64_t)kvh * p.kvh_s;
-    const uint16_t* vh = p.v + (int64_t)kvh * p.kvh_s;
+    const char* kh = reinterpret_cast<const char*>(p.k) + (int64_t)kvh * p.kvh_s * EB;
+    const char* vh = reinterpret_cast<const char*>(p.v) + (int64_t)kvh * p.kvh_s * EB;
 
     // Block ids of the range in windows of 64: lane i holds the id of block
     // b_lo + wbase + i, and the next window is requested one window ahead,
@@ -348,22 +353,39 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
         const int blk = __builtin_amdgcn_readlane(bw, b - b_lo - wbase);
         if ((uint32_t)blk >= p.num_blocks) continue;  // dropped: never dereferenced
         const int nvalid = min(TG, t_end - g * TG);
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh + (int64_t)blk * p.blk_s, rec);
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh + (int64_t)blk * p.blk_s, rec);
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh + (int64_t)blk * p.blk_s * EB, rec);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh + (int64_t)blk * p.blk_s * EB, rec);
         const int soff = slot0 * tok_b;
 
+        // kr: K as BF16 pairs (dims 2j, 2j + 1 in word j); vr: V as loaded
+        // (BF16 pairs, or 4 E4M3 codes per word in words 0 and 1)
         uint32_t kr[U][4], vr[U][4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             // a masked token re-reads the group's first row (always valid),
             // so canary memory past the end never enters the arithmetic
             const uint32_t off = row + ROWS * u < nvalid ? voff[u] : voff0;
-            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, off, soff, PDA_FOLD_AUX);
-            const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, soff, PDA_FOLD_AUX);
+            if constexpr (KV8) {
+                const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(krs, off, soff, PDA_FOLD_AUX);
+                const u32x2 y = __builtin_amdgcn_raw_buffer_load_b64(vrs, off, soff, PDA_FOLD_AUX);
+                // E4M3 -> FP32 -> BF16 is exact (3 mantissa bits, exponents in range)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kr[u][j] = x[j];
-                vr[u][j] = y[j];
+                for (int w = 0; w < 2; ++w) {
+                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[w], false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[w], true);
+                    kr[u][2 * w] = pack_bf16x2(lo[0], lo[1]);
+                    kr[u][2 * w + 1] = pack_bf16x2(hi[0], hi[1]);
+                    vr[u][w] = y[w];
+                }
+                vr[u][2] = vr[u][3] = 0u;
+            } else {
+                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, off, soff, PDA_FOLD_AUX);
+                const u32x4 y = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, soff, PDA_FOLD_AUX);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    kr[u][j] = x[j];
+                    vr[u][j] = y[j];
+                }
             }
         }
 
@@ -446,6 +468,7 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
         }
 
 #if PDA_FOLD_PV_BF16
+        if constexpr (!KV8) {
         // P.V on token pairs: v_dot2 of (p_a, p_b) as BF16 with the two
         // tokens' values of one dim, accumulated in FP32
 #pragma unroll
@@ -466,15 +489,32 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
                 }
             }
         }
+        }
+        if constexpr (KV8) {
 #else
+        {
+#endif
         float vf[U][8];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+            if constexpr (KV8) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                vf[u][2 * j] = bf_lo(vr[u][j]);
-                vf[u][2 * j + 1] = bf_hi(vr[u][j]);
+                for (int w = 0; w < 2; ++w) {
+                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vr[u][w], false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vr[u][w], true);
+                    vf[u][4 * w] = lo[0];
+                    vf[u][4 * w + 1] = lo[1];
+                    vf[u][4 * w + 2] = hi[0];
+                    vf[u][4 * w + 3] = hi[1];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    vf[u][2 * j] = bf_lo(vr[u][j]);
+                    vf[u][2 * j + 1] = bf_hi(vr[u][j]);
+                }
             }
+        }
 #pragma unroll
         for (int h = 0; h < GC; ++h)
 #pragma unroll
@@ -484,8 +524,15 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
                 for (int u = 0; u < U; ++u) acc = fmaf(pa[h * U + u], vf[u][d], acc);
                 o[h][d] = acc;
             }
-#endif
+        }
         wave_lds_sync();  // the next group's partials overwrite this scratch
+    }
+
+    if constexpr (KV8) {   // V = decode(v8) * v_scale: scale o once
+#pragma unroll
+        for (int h = 0; h < GC; ++h)
+#pragma unroll
+            for (int d = 0; d < 8; ++d) o[h][d] *= p.v_scale;
     }
 
     // Wave epilogue, then every contributor's state goes to LDS and one
@@ -740,27 +787,27 @@ __global__ __launch_bounds__(256) void tiled_finalize_kernel(const float* __rest
 
 using FoldFn = void (*)(FoldParams);
 
-template <int MODE, int D>
+template <int MODE, int D, bool KV8>
 FoldFn pick_gc(int gc) {
     switch (gc) {
-        case 1: return fold_kernel<MODE, D, 1>;
-        case 2: return fold_kernel<MODE, D, 2>;
-        case 3: return fold_kernel<MODE, D, 3>;
-        case 4: return fold_kernel<MODE, D, 4>;
-        case 5: return fold_kernel<MODE, D, 5>;
-        case 6: return fold_kernel<MODE, D, 6>;
-        case 7: return fold_kernel<MODE, D, 7>;
-        case 8: return fold_kernel<MODE, D, 8>;
+        case 1: return fold_kernel<MODE, D, 1, KV8>;
+        case 2: return fold_kernel<MODE, D, 2, KV8>;
+        case 3: return fold_kernel<MODE, D, 3, KV8>;
+        case 4: return fold_kernel<MODE, D, 4, KV8>;
+        case 5: return fold_kernel<MODE, D, 5, KV8>;
+        case 6: return fold_kernel<MODE, D, 6, KV8>;
+        case 7: return fold_kernel<MODE, D, 7, KV8>;
+        case 8: return fold_kernel<MODE, D, 8, KV8>;
         default: return nullptr;
     }
 }
 
-template <int MODE>
+template <int MODE, bool KV8>
 FoldFn pick_d(int D, int gc) {
     switch (D) {
-        case 64: return pick_gc<MODE, 64>(gc);
-        case 128: return pick_gc<MODE, 128>(gc);
-        case 256: return pick_gc<MODE, 256>(gc);
+        case 64: return pick_gc<MODE, 64, KV8>(gc);
+        case 128: return pick_gc<MODE, 128, KV8>(gc);
+        case 256: return pick_gc<MODE, 256, KV8>(gc);
         default: return nullptr;
     }
 }
@@ -803,12 +850,16 @@ size_t fold_lds_bytes(int head_dim, int gc, int waves) {
 }
 
 hipError_t launch_fold(int mode, int head_dim, int gc, const FoldParams& p, uint32_t grid_x,
-                       uint32_t grid_y, int waves, hipStream_t stream) {
+                       uint32_t grid_y, int waves, hipStream_t stream, bool kv8) {
     FoldFn fn = nullptr;
     switch (mode) {
-        case kModePartial: fn = pick_d<kModePartial>(head_dim, gc); break;
-        case kModeFinal: fn = pick_d<kModeFinal>(head_dim, gc); break;
-        case kModeTiled: fn = pick_d<kModeTiled>(head_dim, gc); break;
+        case kModePartial:
+            fn = kv8 ? pick_d<kModePartial, true>(head_dim, gc) : pick_d<kModePartial, false>(head_dim, gc);
+            break;
+        case kModeFinal:
+            fn = kv8 ? pick_d<kModeFinal, true>(head_dim, gc) : pick_d<kModeFinal, false>(head_dim, gc);
+            break;
+        case kModeTiled: fn = kv8 ? nullptr : pick_d<kModeTiled, false>(head_dim, gc); break;
         default: break;
     }
     if (!fn || waves < 1 || 64 * waves > fold_max_threads(gc)) return hipErrorInvalidValue;

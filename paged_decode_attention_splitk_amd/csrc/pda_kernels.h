@@ -16,8 +16,8 @@ enum FoldMode : int {
 // Arguments of one fold launch (passed by value as the kernel argument).
 struct FoldParams {
     const uint16_t* q;       // bf16 [S, nq, D]
-    const uint16_t* k;       // bf16 K pool
-    const uint16_t* v;       // bf16 V pool
+    const uint16_t* k;       // K pool: bf16, or E4M3 bytes (FP8 cache)
+    const uint16_t* v;       // V pool, same element type
     const int32_t* tables;   // block tables [S, table_stride] (one-shot) or
                              // tile blocks [S, tile_capacity] (tiled)
     const int32_t* lens;     // seq_lens [S] (one-shot) or tile block counts [S]
@@ -31,7 +31,8 @@ struct FoldParams {
     int bs, table_stride;
     int nsplit;              // splits per sequence (one-shot)
     int lbvs;                // valid slots of a tile's last block (tiled)
-    float c;                 // scale * log2(e)
+    float c;                 // scale * log2(e) (times k_scale for an FP8 cache)
+    float v_scale;           // FP8 cache only: V = decode(v8) * v_scale
 };
 
 // Heads one fold workgroup carries at most (the packed width).
@@ -46,7 +47,7 @@ int fold_max_waves(int gc);
 // Launches the fold kernel for (mode, head_dim, gc) on grid x = `grid_x`,
 // y = number of sequences.  head_dim in {64, 128, 256}, gc in 1..8.
 hipError_t launch_fold(int mode, int head_dim, int gc, const FoldParams& p, uint32_t grid_x,
-                       uint32_t grid_y, int waves, hipStream_t stream);
+                       uint32_t grid_y, int waves, hipStream_t stream, bool kv8 = false);
 
 // Split-K merge: workspace -> bf16 out.
 hipError_t launch_merge(const float* ws, uint16_t* out, uint32_t num_seqs, int nq, int head_dim,

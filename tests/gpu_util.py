@@ -161,3 +161,46 @@ def _read_f32(ptr: int, n: int) -> np.ndarray:
     rc = hip.hipMemcpy(host.ctypes.data, ptr, n * 4, 2)   # hipMemcpyDeviceToHost
     assert rc == 0, rc
     return host
+
+
+def dev_u8(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to("cuda")
+
+
+class PagedFP8OnDevice:
+    """Device copies of a PagedFP8Inputs batch."""
+
+    def __init__(self, inp):
+        self.inp = inp
+        self.q = dev_u16(inp.q)
+        self.k = dev_u8(inp.k8)
+        self.v = dev_u8(inp.v8)
+        self.bt = dev_i32(inp.block_tables)
+        self.lens = dev_i32(inp.seq_lens)
+
+    def run(self, num_splits, rows=None, flags=None, scale=None, k_scale=None, v_scale=None):
+        """Run pda_paged_decode_fp8 (optionally on a subset of sequences);
+        returns (rc, out, ws).  A non-OK return code is returned, not raised."""
+        inp = self.inp
+        q, bt, lens = self.q, self.bt, self.lens
+        if rows is not None:
+            idx = torch.as_tensor(rows, device="cuda", dtype=torch.long)
+            q, bt, lens = q[idx].contiguous(), bt[idx].contiguous(), lens[idx].contiguous()
+        S = q.shape[0]
+        nq, D = inp.num_q_heads, inp.head_dim
+        out = torch.empty((S, nq, D), dtype=torch.bfloat16, device="cuda")
+        wsf = P.pda_workspace_slots(S, nq, num_splits, D) if num_splits > 1 else 0
+        ws = (torch.full((wsf,), float("nan"), dtype=torch.float32, device="cuda")
+              if wsf else None)
+        try:
+            rc = P.pda_paged_decode_fp8(
+                q, self.k, self.v, bt, lens, out, ws, wsf, S, nq, inp.num_kv_heads, D,
+                inp.block_size, bt.shape[1], inp.num_blocks,
+                inp.scale if scale is None else scale,
+                inp.k_scale if k_scale is None else k_scale,
+                inp.v_scale if v_scale is None else v_scale, num_splits,
+                P.PDA_DECODE_UNPACKED if flags is None else flags)
+        except P.PdaError as e:
+            return e.code, out, ws
+        torch.cuda.synchronize()
+        return rc, out, ws

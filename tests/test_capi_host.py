@@ -213,3 +213,38 @@ def test_prefill_gate_and_validation():
         with pytest.raises(P.PdaError) as e:
             pf(**bad)
         assert e.value.code == P.PDA_EINVAL
+
+
+def _decode_fp8(**kw):
+    a = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, block_tables=FAKE, seq_lens=FAKE, out=FAKE,
+             workspace=FAKE, workspace_floats=10**9, num_seqs=2, num_q_heads=8, num_kv_heads=2,
+             head_dim=128, block_size=16, max_blocks_per_seq=8, num_blocks=32, scale=0.1,
+             k_scale=0.01, v_scale=0.02, num_splits=4, flags=0, stream=0)
+    a.update(kw)
+    return P.pda_paged_decode_fp8(**a)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(num_kv_heads=0), dict(num_q_heads=7), dict(head_dim=96), dict(block_size=8),
+    dict(num_splits=0), dict(num_splits=17), dict(workspace=None), dict(workspace_floats=100),
+    dict(q=None), dict(v_cache=None), dict(out=None), dict(k_cache=FAKE + 2), dict(flags=4),
+    dict(scale=float("nan")), dict(k_scale=float("inf")), dict(v_scale=float("nan")),
+])
+def test_decode_fp8_rejects_bad_arguments(bad):
+    with pytest.raises(P.PdaError) as e:
+        _decode_fp8(**bad)
+    assert e.value.code == P.PDA_EINVAL
+    assert P.pda_last_error()
+
+
+def test_decode_fp8_packed_not_applicable_and_empty():
+    # no packed FP8 kernel, even on the packed shape
+    assert _decode_fp8(flags=P.PDA_DECODE_PACKED, num_q_heads=32, num_kv_heads=4,
+                       head_dim=256) == P.PDA_NOT_APPLICABLE
+    assert _decode_fp8(num_seqs=0) == P.PDA_OK
+    assert P.pda_splitk_partials_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10**9, 0, 8, 2, 128, 16,
+                                     8, 32, 0.1, 0.01, 0.02, 2, 0) == P.PDA_OK
+    for bad in (dict(n=1), dict(ks=float("nan"))):
+        with pytest.raises(P.PdaError):
+            P.pda_splitk_partials_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10**9, 2, 8, 2, 128, 16,
+                                      8, 32, 0.1, bad.get("ks", 0.01), 0.02, bad.get("n", 2), 0)
