@@ -284,8 +284,6 @@ def main():
         print(json.dumps(rec), flush=True)
         return
 
-    if args.fp8 and args.packed:
-        sys.exit("--fp8 has no packed kernel")
     inp = (W.make_paged_fp8(args.workload, canary=False) if args.fp8 else
            W.make_paged(args.workload, canary=False))
     k_host, v_host = (inp.k8, inp.v8) if args.fp8 else (inp.k_cache, inp.v_cache)
@@ -327,7 +325,7 @@ def main():
             else:
                 P.pda_splitk_partials_fp8(q, ks[i % copies], vs[i % copies], bt, lens, ws, wsf,
                                           S, nq, nkv, D, bs, mb, inp.num_blocks, inp.scale,
-                                          inp.k_scale, inp.v_scale, n, sp)
+                                          inp.k_scale, inp.v_scale, n, flags, sp)
         elif n == 1:
             rc = P.pda_paged_decode(q, ks[i % copies], vs[i % copies], bt, lens, out, None, 0, S,
                                     nq, nkv, D, bs, mb, inp.num_blocks, inp.scale, 1, flags, sp)
@@ -415,7 +413,8 @@ def main():
         "kernels_us": {"splitk_fold": round(fold_avg * 1e3, 2),
                        "splitk_merge": round(merge_avg * 1e3, 2)},
         "roofline": {
-            "kernel": (f"GQA-packed MFMA decode (packed_kernel<{'true' if n > 1 else 'false'}>)"
+            "kernel": (f"GQA-packed MFMA decode (packed_kernel<{'true' if n > 1 else 'false'}, W, "
+                       f"{'true' if args.fp8 else 'false'}>)"
                        if args.packed else
                        f"split-K fold (fold_kernel<{0 if n > 1 else 1},{D},{min(nq // nkv, 8)},"
                        f"{'true' if args.fp8 else 'false'}>)"),

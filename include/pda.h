@@ -138,10 +138,13 @@ uint32_t pda_split_chunk(uint32_t seq_len, uint32_t num_splits, uint32_t block_s
  *                     V = decode(v) * v_scale (scores are
  *                     scale * q . K; the workspace partials hold o of the
  *                     scaled V)
- *   flags             PDA_DECODE_UNPACKED or PDA_DECODE_DEFAULT; there is no
- *                     packed FP8 kernel (PDA_DECODE_PACKED: NOT_APPLICABLE)
- * q stays BF16 and out is BF16; the caches need 8-byte alignment (16 is what
- * pda_paged_decode asks and is checked the same way).
+ *   flags             as for pda_paged_decode: the GQA-packed MFMA kernel
+ *                     has an FP8 form (the page names a BF16 and an FP8
+ *                     packed source), with the same gate, and
+ *                     PDA_DECODE_DEFAULT arms it on non-split launches when
+ *                     pda_gqa_pack_enabled() says so
+ * q stays BF16 and out is BF16; the caches are checked for the same
+ * alignment as pda_paged_decode's.
  * ------------------------------------------------------------------------ */
 int pda_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* seq_lens, void* out,
@@ -152,14 +155,15 @@ int pda_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache
                          uint32_t flags, void* stream);
 
 /* pda_paged_decode_fp8 without the merge (num_splits >= 2): leaves the
- * partials in the workspace; pda_splitk_merge finishes them. */
+ * partials in the workspace; pda_splitk_merge finishes them.  flags as for
+ * pda_splitk_partials. */
 int pda_splitk_partials_fp8(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, const int32_t* seq_lens,
                             float* workspace, uint64_t workspace_floats, uint32_t num_seqs,
                             uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
                             uint32_t block_size, uint32_t max_blocks_per_seq,
                             uint32_t num_blocks, float scale, float k_scale, float v_scale,
-                            uint32_t num_splits, void* stream);
+                            uint32_t num_splits, uint32_t flags, void* stream);
 
 /* ------------------------------------------------------------------------
  * Causal paged prefill (prefill page "prefill_attn_fa128.rs": `applies` and

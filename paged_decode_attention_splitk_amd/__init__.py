@@ -101,7 +101,8 @@ _SIGS = {
     "pda_paged_decode_fp8": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _u64, _u32, _u32, _u32,
                                     _u32, _u32, _u32, _u32, _f32, _f32, _f32, _u32, _u32, _vp]),
     "pda_splitk_partials_fp8": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _u64, _u32, _u32, _u32,
-                                       _u32, _u32, _u32, _u32, _f32, _f32, _f32, _u32, _vp]),
+                                       _u32, _u32, _u32, _u32, _f32, _f32, _f32, _u32, _u32,
+                                       _vp]),
     "pda_prefill_applies": (_int, [_u32, _u32, _u32, _int, _u32]),
     "pda_paged_prefill": (_int, [_vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _u32, _u32, _u32,
                                  _u32, _u32, _u32, _u32, _f32, _vp]),
@@ -280,11 +281,11 @@ def pda_paged_decode_fp8(q, k_cache, v_cache, block_tables, seq_lens, out, works
 def pda_splitk_partials_fp8(q, k_cache, v_cache, block_tables, seq_lens, workspace,
                             workspace_floats, num_seqs, num_q_heads, num_kv_heads, head_dim,
                             block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale,
-                            num_splits, stream=None) -> int:
+                            num_splits, flags=PDA_DECODE_UNPACKED, stream=None) -> int:
     return _check(_lib.pda_splitk_partials_fp8(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         _ptr(workspace), workspace_floats, num_seqs, num_q_heads, num_kv_heads, head_dim,
-        block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, num_splits,
+        block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, num_splits, flags,
         _stream(stream)))
 
 

@@ -186,12 +186,19 @@ pda::PackedParams packed_params(const DecodeShape& s, const void* q, const void*
     return p;
 }
 
-// kv8: the caches hold OCP E4M3 bytes with per-tensor scales k_scale / v_scale
-// (the fold kernel's FP8 form; never packed).
+// The element type of the K/V caches: BF16, or OCP E4M3 bytes with
+// per-tensor scales (K = decode(k) * k_scale, V = decode(v) * v_scale).
+struct KvType {
+    bool fp8;
+    float k_scale, v_scale;
+};
+constexpr KvType kBf16Kv{false, 1.f, 1.f};
+
 int run_partials(const DecodeShape& s, const void* q, const void* k, const void* v,
                  const int32_t* bt, const int32_t* lens, float* ws, uint64_t ws_floats,
                  float scale, uint32_t nsplit, bool packed, hipStream_t stream,
-                 bool kv8 = false, float k_scale = 1.f, float v_scale = 1.f) {
+                 const KvType& kv) {
+    const float sc = kv.fp8 ? scale * kv.k_scale : scale;   // k_scale joins the score factor
     if (!ws) return fail(PDA_EINVAL, "workspace is NULL with num_splits > 1");
     if (!aligned(ws, 8)) return fail(PDA_EINVAL, "workspace must be 8-byte aligned");
     const uint64_t need = pda_workspace_slots(s.num_seqs, s.nq, nsplit, s.D);
@@ -199,24 +206,107 @@ int run_partials(const DecodeShape& s, const void* q, const void* k, const void*
         return fail(PDA_EINVAL, "workspace holds %llu floats, needs %llu",
                     (unsigned long long)ws_floats, (unsigned long long)need);
     if (packed) {
-        pda::PackedParams p = packed_params(s, q, k, v, bt, lens, scale, nsplit);
+        pda::PackedParams p = packed_params(s, q, k, v, bt, lens, sc, nsplit);
         p.ws = ws;
-        hipError_t e = pda::launch_packed(p, s.num_seqs, stream);
+        p.v_scale = kv.v_scale;
+        hipError_t e = pda::launch_packed(p, s.num_seqs, stream, kv.fp8);
         if (e != hipSuccess) return hip_fail(e, "packed split-K partial launch");
         return PDA_OK;
     }
     int hg = 0;
     const int gc = head_groups(s.nq / s.nkv, &hg);
-    pda::FoldParams p = fold_params(s, q, k, v, bt, lens, hg, kv8 ? scale * k_scale : scale,
-                                    nsplit);
+    pda::FoldParams p = fold_params(s, q, k, v, bt, lens, hg, sc, nsplit);
     p.ws = ws;
-    p.v_scale = v_scale;
+    p.v_scale = kv.v_scale;
     const int waves = oneshot_waves(s.nkv, nsplit, s.D, gc);
     const uint64_t gx = (uint64_t)s.nkv * hg * nsplit;
     hipError_t e = pda::launch_fold(pda::kModePartial, (int)s.D, gc, p, (uint32_t)gx, s.num_seqs,
-                                    waves, stream, kv8);
+                                    waves, stream, kv.fp8);
     if (e != hipSuccess) return hip_fail(e, "split-K partial launch");
     return PDA_OK;
+}
+
+bool scales_finite(float scale, const KvType& kv) {
+    return std::isfinite(scale) && std::isfinite(kv.k_scale) && std::isfinite(kv.v_scale);
+}
+
+const char* const kPackNotApplicable =
+    "packed kernel not applicable: needs num_q_heads == 8 * num_kv_heads and head_dim 256";
+
+// pda_splitk_partials and its FP8 form.
+int partials_impl(const DecodeShape& s, const void* q, const void* k, const void* v,
+                  const int32_t* bt, const int32_t* lens, float* ws, uint64_t ws_floats,
+                  float scale, uint32_t nsplit, uint32_t flags, hipStream_t stream,
+                  const KvType& kv) {
+    int rc = check_decode(s, q, k, v, bt, lens, nullptr, false);
+    if (rc != PDA_OK) return rc;
+    if (flags > PDA_DECODE_DEFAULT) return fail(PDA_EINVAL, "unknown flags 0x%x", flags);
+    if (nsplit < 2 || nsplit > pda::kMaxDecodeSplits)
+        return fail(PDA_EINVAL, "num_splits %u outside 2..%u for a partials launch", nsplit,
+                    pda::kMaxDecodeSplits);
+    if (!scales_finite(scale, kv)) return fail(PDA_EINVAL, "scale (or an FP8 scale) is not finite");
+    const bool packed = flags == PDA_DECODE_PACKED;
+    if (packed && !pda_gqa_pack_shape_ok(s.nq, s.nkv, s.D)) {
+        g_last_error = kPackNotApplicable;
+        return PDA_NOT_APPLICABLE;
+    }
+    if (s.num_seqs == 0) return ok();
+    rc = run_partials(s, q, k, v, bt, lens, ws, ws_floats, scale, nsplit, packed, stream, kv);
+    return rc == PDA_OK ? ok() : rc;
+}
+
+// pda_paged_decode and its FP8 form.
+int decode_impl(const DecodeShape& s, const void* q, const void* k, const void* v,
+                const int32_t* bt, const int32_t* lens, void* out, float* ws,
+                uint64_t ws_floats, float scale, uint32_t nsplit, uint32_t flags,
+                hipStream_t st, const KvType& kv) {
+    int rc = check_decode(s, q, k, v, bt, lens, out, true);
+    if (rc != PDA_OK) return rc;
+    if (flags > PDA_DECODE_DEFAULT) return fail(PDA_EINVAL, "unknown flags 0x%x", flags);
+    if (nsplit < 1 || nsplit > pda::kMaxDecodeSplits)
+        return fail(PDA_EINVAL, "num_splits %u outside 1..%u", nsplit, pda::kMaxDecodeSplits);
+    if (!scales_finite(scale, kv)) return fail(PDA_EINVAL, "scale (or an FP8 scale) is not finite");
+
+    const bool shape_packs = pda_gqa_pack_shape_ok(s.nq, s.nkv, s.D);
+    // the default arms the packed kernel on non-split launches only, as the
+    // pages do (for BF16 and FP8 caches alike); an explicit request also
+    // takes it with split-K
+    if (flags == PDA_DECODE_DEFAULT)
+        flags = shape_packs && nsplit == 1 && pda_gqa_pack_enabled() ? PDA_DECODE_PACKED
+                                                                     : PDA_DECODE_UNPACKED;
+    const bool packed = flags == PDA_DECODE_PACKED;
+    if (packed && !shape_packs) {
+        g_last_error = kPackNotApplicable;
+        return PDA_NOT_APPLICABLE;
+    }
+    if (s.num_seqs == 0) return ok();
+    const float sc = kv.fp8 ? scale * kv.k_scale : scale;
+    if (packed && nsplit == 1) {
+        pda::PackedParams p = packed_params(s, q, k, v, bt, lens, sc, 1);
+        p.out = static_cast<uint16_t*>(out);
+        p.v_scale = kv.v_scale;
+        hipError_t e = pda::launch_packed(p, s.num_seqs, st, kv.fp8);
+        if (e != hipSuccess) return hip_fail(e, "packed decode launch");
+        return ok();
+    }
+    if (nsplit == 1) {
+        int hg = 0;
+        const int gc = head_groups(s.nq / s.nkv, &hg);
+        pda::FoldParams p = fold_params(s, q, k, v, bt, lens, hg, sc, 1);
+        p.out = static_cast<uint16_t*>(out);
+        p.v_scale = kv.v_scale;
+        const int waves = oneshot_waves(s.nkv, 1, s.D, gc);
+        hipError_t e = pda::launch_fold(pda::kModeFinal, (int)s.D, gc, p, s.nkv * (uint32_t)hg,
+                                        s.num_seqs, waves, st, kv.fp8);
+        if (e != hipSuccess) return hip_fail(e, "single-split decode launch");
+        return ok();
+    }
+    rc = run_partials(s, q, k, v, bt, lens, ws, ws_floats, scale, nsplit, packed, st, kv);
+    if (rc != PDA_OK) return rc;
+    hipError_t e = pda::launch_merge(ws, static_cast<uint16_t*>(out), s.num_seqs, (int)s.nq,
+                                     (int)s.D, (int)nsplit, st);
+    if (e != hipSuccess) return hip_fail(e, "split-K merge launch");
+    return ok();
 }
 
 }  // namespace
@@ -242,23 +332,9 @@ int pda_splitk_partials(const void* q, const void* k_cache, const void* v_cache,
                         uint32_t num_splits, uint32_t flags, void* stream) {
     const DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim,
                         block_size, max_blocks_per_seq, num_blocks};
-    int rc = check_decode(s, q, k_cache, v_cache, block_tables, seq_lens, nullptr, false);
-    if (rc != PDA_OK) return rc;
-    if (flags > PDA_DECODE_DEFAULT) return fail(PDA_EINVAL, "unknown flags 0x%x", flags);
-    if (num_splits < 2 || num_splits > pda::kMaxDecodeSplits)
-        return fail(PDA_EINVAL, "num_splits %u outside 2..%u for a partials launch", num_splits,
-                    pda::kMaxDecodeSplits);
-    if (!std::isfinite(scale)) return fail(PDA_EINVAL, "scale is not finite");
-    const bool packed = flags == PDA_DECODE_PACKED;
-    if (packed && !pda_gqa_pack_shape_ok(num_q_heads, num_kv_heads, head_dim)) {
-        g_last_error = "packed kernel not applicable: needs num_q_heads == 8 * num_kv_heads "
-                       "and head_dim 256";
-        return PDA_NOT_APPLICABLE;
-    }
-    if (num_seqs == 0) return ok();
-    rc = run_partials(s, q, k_cache, v_cache, block_tables, seq_lens, workspace, workspace_floats,
-                      scale, num_splits, packed, (hipStream_t)stream);
-    return rc == PDA_OK ? ok() : rc;
+    return partials_impl(s, q, k_cache, v_cache, block_tables, seq_lens, workspace,
+                         workspace_floats, scale, num_splits, flags, (hipStream_t)stream,
+                         kBf16Kv);
 }
 
 int pda_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -270,39 +346,9 @@ int pda_paged_decode_fp8(const void* q, const void* k_cache, const void* v_cache
                          uint32_t flags, void* stream) {
     const DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim,
                         block_size, max_blocks_per_seq, num_blocks};
-    int rc = check_decode(s, q, k_cache, v_cache, block_tables, seq_lens, out, true);
-    if (rc != PDA_OK) return rc;
-    if (flags > PDA_DECODE_DEFAULT) return fail(PDA_EINVAL, "unknown flags 0x%x", flags);
-    if (num_splits < 1 || num_splits > pda::kMaxDecodeSplits)
-        return fail(PDA_EINVAL, "num_splits %u outside 1..%u", num_splits, pda::kMaxDecodeSplits);
-    if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
-        return fail(PDA_EINVAL, "scale, k_scale and v_scale must be finite");
-    if (flags == PDA_DECODE_PACKED) {
-        g_last_error = "no packed kernel for an FP8 cache";
-        return PDA_NOT_APPLICABLE;
-    }
-    if (num_seqs == 0) return ok();
-    hipStream_t st = (hipStream_t)stream;
-    if (num_splits == 1) {
-        int hg = 0;
-        const int gc = head_groups(num_q_heads / num_kv_heads, &hg);
-        pda::FoldParams p = fold_params(s, q, k_cache, v_cache, block_tables, seq_lens, hg,
-                                        scale * k_scale, 1);
-        p.out = static_cast<uint16_t*>(out);
-        p.v_scale = v_scale;
-        const int waves = oneshot_waves(num_kv_heads, 1, head_dim, gc);
-        hipError_t e = pda::launch_fold(pda::kModeFinal, (int)head_dim, gc, p,
-                                        (uint32_t)(num_kv_heads * hg), num_seqs, waves, st, true);
-        if (e != hipSuccess) return hip_fail(e, "single-split FP8 decode launch");
-        return ok();
-    }
-    rc = run_partials(s, q, k_cache, v_cache, block_tables, seq_lens, workspace, workspace_floats,
-                      scale, num_splits, false, st, true, k_scale, v_scale);
-    if (rc != PDA_OK) return rc;
-    hipError_t e = pda::launch_merge(workspace, static_cast<uint16_t*>(out), num_seqs,
-                                     (int)num_q_heads, (int)head_dim, (int)num_splits, st);
-    if (e != hipSuccess) return hip_fail(e, "split-K merge launch");
-    return ok();
+    return decode_impl(s, q, k_cache, v_cache, block_tables, seq_lens, out, workspace,
+                       workspace_floats, scale, num_splits, flags, (hipStream_t)stream,
+                       KvType{true, k_scale, v_scale});
 }
 
 int pda_splitk_partials_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -311,20 +357,12 @@ int pda_splitk_partials_fp8(const void* q, const void* k_cache, const void* v_ca
                             uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
                             uint32_t block_size, uint32_t max_blocks_per_seq,
                             uint32_t num_blocks, float scale, float k_scale, float v_scale,
-                            uint32_t num_splits, void* stream) {
+                            uint32_t num_splits, uint32_t flags, void* stream) {
     const DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim,
                         block_size, max_blocks_per_seq, num_blocks};
-    int rc = check_decode(s, q, k_cache, v_cache, block_tables, seq_lens, nullptr, false);
-    if (rc != PDA_OK) return rc;
-    if (num_splits < 2 || num_splits > pda::kMaxDecodeSplits)
-        return fail(PDA_EINVAL, "num_splits %u outside 2..%u for a partials launch", num_splits,
-                    pda::kMaxDecodeSplits);
-    if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
-        return fail(PDA_EINVAL, "scale, k_scale and v_scale must be finite");
-    if (num_seqs == 0) return ok();
-    rc = run_partials(s, q, k_cache, v_cache, block_tables, seq_lens, workspace, workspace_floats,
-                      scale, num_splits, false, (hipStream_t)stream, true, k_scale, v_scale);
-    return rc == PDA_OK ? ok() : rc;
+    return partials_impl(s, q, k_cache, v_cache, block_tables, seq_lens, workspace,
+                         workspace_floats, scale, num_splits, flags, (hipStream_t)stream,
+                         KvType{true, k_scale, v_scale});
 }
 
 int pda_prefill_applies(uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
@@ -408,54 +446,9 @@ int pda_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                      float scale, uint32_t num_splits, uint32_t flags, void* stream) {
     const DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim,
                         block_size, max_blocks_per_seq, num_blocks};
-    int rc = check_decode(s, q, k_cache, v_cache, block_tables, seq_lens, out, true);
-    if (rc != PDA_OK) return rc;
-    if (flags > PDA_DECODE_DEFAULT) return fail(PDA_EINVAL, "unknown flags 0x%x", flags);
-    if (num_splits < 1 || num_splits > pda::kMaxDecodeSplits)
-        return fail(PDA_EINVAL, "num_splits %u outside 1..%u", num_splits, pda::kMaxDecodeSplits);
-    if (!std::isfinite(scale)) return fail(PDA_EINVAL, "scale is not finite");
-    hipStream_t st = (hipStream_t)stream;
-
-    const bool shape_packs = pda_gqa_pack_shape_ok(num_q_heads, num_kv_heads, head_dim);
-    // the default arms the packed kernel on non-split launches only, as the
-    // pages do; an explicit request also takes it with split-K
-    if (flags == PDA_DECODE_DEFAULT)
-        flags = shape_packs && num_splits == 1 && pda_gqa_pack_enabled() ? PDA_DECODE_PACKED
-                                                                          : PDA_DECODE_UNPACKED;
-    const bool packed = flags == PDA_DECODE_PACKED;
-    if (packed && !shape_packs) {
-        g_last_error = "packed kernel not applicable: needs num_q_heads == 8 * num_kv_heads "
-                       "and head_dim 256";
-        return PDA_NOT_APPLICABLE;
-    }
-    if (num_seqs == 0) return ok();
-    if (packed && num_splits == 1) {
-        pda::PackedParams p = packed_params(s, q, k_cache, v_cache, block_tables, seq_lens,
-                                            scale, 1);
-        p.out = static_cast<uint16_t*>(out);
-        hipError_t e = pda::launch_packed(p, num_seqs, st);
-        if (e != hipSuccess) return hip_fail(e, "packed decode launch");
-        return ok();
-    }
-    if (num_splits == 1) {
-        int hg = 0;
-        const int gc = head_groups(num_q_heads / num_kv_heads, &hg);
-        pda::FoldParams p =
-            fold_params(s, q, k_cache, v_cache, block_tables, seq_lens, hg, scale, 1);
-        p.out = static_cast<uint16_t*>(out);
-        const int waves = oneshot_waves(num_kv_heads, 1, head_dim, gc);
-        hipError_t e = pda::launch_fold(pda::kModeFinal, (int)head_dim, gc, p,
-                                        (uint32_t)(num_kv_heads * hg), num_seqs, waves, st);
-        if (e != hipSuccess) return hip_fail(e, "single-split decode launch");
-        return ok();
-    }
-    rc = run_partials(s, q, k_cache, v_cache, block_tables, seq_lens, workspace, workspace_floats,
-                      scale, num_splits, packed, st);
-    if (rc != PDA_OK) return rc;
-    hipError_t e = pda::launch_merge(workspace, static_cast<uint16_t*>(out), num_seqs,
-                                     (int)num_q_heads, (int)head_dim, (int)num_splits, st);
-    if (e != hipSuccess) return hip_fail(e, "split-K merge launch");
-    return ok();
+    return decode_impl(s, q, k_cache, v_cache, block_tables, seq_lens, out, workspace,
+                       workspace_floats, scale, num_splits, flags, (hipStream_t)stream,
+                       kBf16Kv);
 }
 
 // ---------------------------------------------------------------------------

@@ -21,6 +21,13 @@
 // groups.  W waves take 16-token tiles round-robin; their states are merged
 // through LDS in wave order at the end.
 //
+// The FP8 form (KV8 = true) reads OCP E4M3 caches (the page names a BF16
+// and an FP8 packed source): codes are decoded exactly to BF16 in registers
+// (K before the A operand, V before its LDS tile), so the matrix products
+// are the BF16 ones; k_scale is part of the score factor c and v_scale
+// multiplies o once at the end.  To read K in 16-byte pieces, the FP8 form
+// orders the contraction differently (see kdim): q follows the same order.
+//
 // The split-K form (SPLIT = true) takes one split of the sequence per
 // workgroup, with the split partition of the unpacked kernels, and leaves
 // each head's FP32 (o unnormalised, m natural-log, l) in the split-K
@@ -49,6 +56,7 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -57,6 +65,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     v[0] = (__bf16)a;
     v[1] = (__bf16)b;
     return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight E4M3 codes (w0 bytes 0..3, then w1 bytes 0..3) as eight BF16 values
+// in the same order; exact (3 mantissa bits, every exponent in range).
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+    return u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
+                   pack_bf16x2(d[0], d[1])};
+}
+
+// First of the 8 consecutive head dims that lanes of 16-lane group g hold
+// in k-step kb of S^T = K . Q^T.  BF16: 32 kb + 8 g (one 16-byte K piece per
+// step).  FP8: 64 (kb / 2) + 16 g + 8 (kb % 2), so one 16-byte load of 16
+// codes feeds steps 2j and 2j + 1.  Any order is the same sum as long as K
+// and q agree.
+template <bool KV8>
+__device__ __forceinline__ int kdim(int kb, int g) {
+    return KV8 ? 64 * (kb >> 1) + 16 * g + 8 * (kb & 1) : 32 * kb + 8 * g;
 }
 
 // Values of the lower and upper 32-lane halves, and of the even and odd
@@ -128,8 +157,9 @@ __device__ __forceinline__ void packed_seq_of_rank(const int32_t* __restrict__ l
 
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <bool SPLIT, int W>
+template <bool SPLIT, int W, bool KV8>
 __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p) {
+    constexpr int EB = KV8 ? 1 : 2;   // bytes per cache element
     extern __shared__ __align__(16) uint16_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -167,8 +197,8 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
         const int hq = c < kG ? c : 0;
-        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(p.q + (q_row + hq) * kD + kb * 32 +
-                                                           g * 8);
+        const u32x4_t w =
+            *reinterpret_cast<const u32x4_t*>(p.q + (q_row + hq) * kD + kdim<KV8>(kb, g));
         const u32x4_t z = {0u, 0u, 0u, 0u};
         qb[kb] = __builtin_bit_cast(bf16x8_t, c < kG ? w : z);
     }
@@ -180,8 +210,9 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
 
     uint16_t* vt = smem + wave * kVTileElems;
     const int32_t* blocks = p.tables + (int64_t)seq * p.table_stride;
-    const uint16_t* kbase = p.k + (int64_t)kvh * p.kvh_s;
-    const uint16_t* vbase = p.v + (int64_t)kvh * p.kvh_s;
+    const char* kbase = reinterpret_cast<const char*>(p.k) + (int64_t)kvh * p.kvh_s * EB;
+    const char* vbase = reinterpret_cast<const char*>(p.v) + (int64_t)kvh * p.kvh_s * EB;
+    const int64_t tok_b = p.tok_s * EB;
     // t_begin is a block boundary, and blocks hold whole tiles
     const int t_first = t_begin / kTile;
     const int t_last = (t_end + kTile - 1) / kTile;
@@ -207,25 +238,38 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
         const int blk = __builtin_amdgcn_readlane(bw, b - b_lo - wbase);
         if ((uint32_t)blk >= p.num_blocks) continue;  // dropped: never dereferenced
         const int nvalid = min(kTile, t_end - tok0);
-        const uint16_t* kblk = kbase + (int64_t)blk * p.blk_s + (int64_t)slot0 * p.tok_s;
-        const uint16_t* vblk = vbase + (int64_t)blk * p.blk_s + (int64_t)slot0 * p.tok_s;
+        const char* kblk = kbase + ((int64_t)blk * p.blk_s + (int64_t)slot0 * p.tok_s) * EB;
+        const char* vblk = vbase + ((int64_t)blk * p.blk_s + (int64_t)slot0 * p.tok_s) * EB;
 
         // K as the A operand (lane = token c); a masked token re-reads the
         // tile's first row, so canary memory never enters the arithmetic
         const int tk = c < nvalid ? c : 0;
         bf16x8_t ka[8];
+        if constexpr (KV8) {
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-            ka[kb] = __builtin_bit_cast(
-                bf16x8_t, *reinterpret_cast<const u32x4_t*>(kblk + (int64_t)tk * p.tok_s +
-                                                            kb * 32 + g * 8));
-        // V rows in natural order: load i covers tokens 2i and 2i + 1
-        u32x4_t vr[8];
+            for (int j = 0; j < 4; ++j) {
+                const u32x4_t x =
+                    *reinterpret_cast<const u32x4_t*>(kblk + tk * tok_b + 64 * j + 16 * g);
+                ka[2 * j] = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16(x[0], x[1]));
+                ka[2 * j + 1] = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16(x[2], x[3]));
+            }
+        } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = 2 * i + (lane >> 5);
+            for (int kb = 0; kb < 8; ++kb)
+                ka[kb] = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const u32x4_t*>(kblk + tk * tok_b +
+                                                                2 * kdim<KV8>(kb, g)));
+        }
+        // V rows in natural order: BF16 load i covers tokens 2i and 2i + 1
+        // (8 dims a lane), FP8 load i tokens 4i .. 4i + 3 (16 dims a lane)
+        constexpr int NV = KV8 ? 4 : 8;
+        u32x4_t vr[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int row = KV8 ? 4 * i + (lane >> 4) : 2 * i + (lane >> 5);
             const int tv = row < nvalid ? row : 0;
-            vr[i] = *reinterpret_cast<const u32x4_t*>(vblk + (int64_t)tv * p.tok_s + (lane & 31) * 8);
+            const int col_b = KV8 ? (lane & 15) * 16 : (lane & 31) * 16;
+            vr[i] = *reinterpret_cast<const u32x4_t*>(vblk + tv * tok_b + col_b);
         }
 
         // S^T = K . Q^T ; acc[r] = score of token 4g + r for head c
@@ -253,10 +297,22 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
             s16x4_t, uint64_t(pack_bf16x2(pr[0], pr[1])) | (uint64_t(pack_bf16x2(pr[2], pr[3])) << 32));
 
         // V tile -> LDS (swizzled rows), then rescale o while the writes land
+        if constexpr (KV8) {
+            // dims 16 q .. 16 q + 15 (q = lane & 15) are chunks 4q .. 4q + 3,
+            // which the swizzle keeps contiguous (it flips chunk bits 2..4)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = 2 * i + (lane >> 5);
-            *reinterpret_cast<u32x4_t*>(vt + vchunk(row, 2 * (lane & 31))) = vr[i];
+            for (int i = 0; i < NV; ++i) {
+                const int row = 4 * i + (lane >> 4);
+                uint16_t* dst = vt + vchunk(row, 4 * (lane & 15));
+                *reinterpret_cast<u32x4_t*>(dst) = fp8x8_to_bf16(vr[i][0], vr[i][1]);
+                *reinterpret_cast<u32x4_t*>(dst + 8) = fp8x8_to_bf16(vr[i][2], vr[i][3]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int row = 2 * i + (lane >> 5);
+                *reinterpret_cast<u32x4_t*>(vt + vchunk(row, 2 * (lane & 31))) = vr[i];
+            }
         }
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
             // O rows are heads 4g + r; their factor lives in lane 4g + r
@@ -282,6 +338,13 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
             O[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, O[nb], 0, 0, 0);
         }
         wave_lds_sync();  // the next tile overwrites this wave's V tile
+    }
+
+    if constexpr (KV8) {   // V = decode(v) * v_scale: scale o once
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[nb][r] *= p.v_scale;
     }
 
     // Merge the waves in order.  LDS (reusing the V tiles): per wave and
@@ -335,9 +398,8 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
     }
 }
 
-}  // namespace
-
-hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream) {
+template <bool KV8>
+hipError_t launch_packed_t(const PackedParams& p, uint32_t num_seqs, hipStream_t stream) {
     if (p.nsplit > 1) {
         // A split holds about 1/nsplit of a sequence: the more splits, the
         // fewer tiles each item has, and the fewer waves pay off (measured
@@ -348,17 +410,25 @@ hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t s
         const int w = p.nsplit >= 12 ? 2 : (p.nsplit >= 3 ? 4 : 8);
         const size_t lds = sizeof(uint16_t) * (size_t)w * kVTileElems;
         if (w == 2)
-            hipLaunchKernelGGL((packed_kernel<true, 2>), grid, dim3(128), lds, stream, p);
+            hipLaunchKernelGGL((packed_kernel<true, 2, KV8>), grid, dim3(128), lds, stream, p);
         else if (w == 4)
-            hipLaunchKernelGGL((packed_kernel<true, 4>), grid, dim3(256), lds, stream, p);
+            hipLaunchKernelGGL((packed_kernel<true, 4, KV8>), grid, dim3(256), lds, stream, p);
         else
-            hipLaunchKernelGGL((packed_kernel<true, 8>), grid, dim3(512), lds, stream, p);
+            hipLaunchKernelGGL((packed_kernel<true, 8, KV8>), grid, dim3(512), lds, stream, p);
     } else {
         const size_t lds = sizeof(uint16_t) * (size_t)kWaves * kVTileElems;   // 64 KiB
-        hipLaunchKernelGGL((packed_kernel<false, kWaves>), dim3((uint32_t)p.nkv, num_seqs),
+        hipLaunchKernelGGL((packed_kernel<false, kWaves, KV8>), dim3((uint32_t)p.nkv, num_seqs),
                            dim3(64 * kWaves), lds, stream, p);
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream,
+                         bool kv8) {
+    return kv8 ? launch_packed_t<true>(p, num_seqs, stream)
+               : launch_packed_t<false>(p, num_seqs, stream);
 }
 
 }  // namespace pda

@@ -74,9 +74,12 @@ struct PackedParams {
     int nq, nkv;
     int bs, table_stride;
     int nsplit;
-    float c;                 // scale * log2(e)
+    float c;                 // scale * log2(e) (times k_scale for an FP8 cache)
+    float v_scale;           // FP8 cache: V = decode(v) * v_scale
 };
-hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream);
+// kv8: k and v hold OCP E4M3 bytes (strides in bytes).
+hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream,
+                         bool kv8 = false);
 
 // Causal paged prefill of one sequence, head_dim 256 (MFMA).
 struct PrefillParams {

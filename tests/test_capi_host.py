@@ -238,13 +238,18 @@ def test_decode_fp8_rejects_bad_arguments(bad):
 
 
 def test_decode_fp8_packed_not_applicable_and_empty():
-    # no packed FP8 kernel, even on the packed shape
-    assert _decode_fp8(flags=P.PDA_DECODE_PACKED, num_q_heads=32, num_kv_heads=4,
-                       head_dim=256) == P.PDA_NOT_APPLICABLE
+    # the packed FP8 kernel has the BF16 one's gate
+    assert _decode_fp8(flags=P.PDA_DECODE_PACKED) == P.PDA_NOT_APPLICABLE
+    assert _decode_fp8(flags=P.PDA_DECODE_PACKED, num_q_heads=24, num_kv_heads=4,
+                       head_dim=256, num_splits=1) == P.PDA_NOT_APPLICABLE
+    assert P.pda_splitk_partials_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10**9, 2, 8, 2, 128, 16,
+                                     8, 32, 0.1, 0.01, 0.02, 2, P.PDA_DECODE_PACKED,
+                                     0) == P.PDA_NOT_APPLICABLE
     assert _decode_fp8(num_seqs=0) == P.PDA_OK
     assert P.pda_splitk_partials_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10**9, 0, 8, 2, 128, 16,
-                                     8, 32, 0.1, 0.01, 0.02, 2, 0) == P.PDA_OK
+                                     8, 32, 0.1, 0.01, 0.02, 2, 0, 0) == P.PDA_OK
     for bad in (dict(n=1), dict(ks=float("nan"))):
         with pytest.raises(P.PdaError):
             P.pda_splitk_partials_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10**9, 2, 8, 2, 128, 16,
-                                      8, 32, 0.1, bad.get("ks", 0.01), 0.02, bad.get("n", 2), 0)
+                                      8, 32, 0.1, bad.get("ks", 0.01), 0.02, bad.get("n", 2), 0,
+                                      0)

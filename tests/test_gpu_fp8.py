@@ -157,7 +157,7 @@ def test_batch_invariance():
 
 
 def test_flags():
-    f = W.make_paged_fp8("tiny", canary=True)
+    f = W.make_paged_fp8("tiny", canary=True)   # 8 q / 2 kv heads, D 128: no packing
     dev = PagedFP8OnDevice(f)
     rc, _, _ = dev.run(4, flags=P.PDA_DECODE_PACKED)
     assert rc == P.PDA_NOT_APPLICABLE
@@ -165,3 +165,49 @@ def test_flags():
     assert rc == P.PDA_OK
     _, out_u, _ = dev.run(4)
     assert np.array_equal(host_bits(out_d), host_bits(out_u))
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_packed_fp8_edges(bs):
+    """The GQA-packed MFMA kernel's FP8 form (8 q heads x head_dim 256 per
+    workgroup), one split and split-K, on edge lengths."""
+    lens = (0, 1, 15, 16, 17, 100, 333, 2000)
+    say(f"[fp8 packed edges] bs={bs}")
+    base = W.Workload(name="pedge8", seed=21, num_seqs=len(lens), num_q_heads=16,
+                      num_kv_heads=2, head_dim=256, block_size=bs, seq_lens=lens)
+    f = W.make_paged_fp8(base, canary=True, k_scale=0.011, v_scale=0.017)
+    dev = PagedFP8OnDevice(f)
+    ref = _ref(f)
+    for n in (1, 2, 5, 16):
+        rc, out, _ = dev.run(n, flags=P.PDA_DECODE_PACKED)
+        assert rc == P.PDA_OK
+        assert_out_close(host_bf16(out), ref, f"packed fp8 n={n}")
+        assert np.all(host_bits(out)[0] == 0)
+
+
+def test_packed_fp8_partials_and_invariance():
+    """Packed FP8 split-K partials with power-of-two scales against the BF16
+    oracle's partials on the same (exact) values; batch invariance."""
+    base = W.Workload(name="ppart8", seed=22, num_seqs=6, num_q_heads=32, num_kv_heads=4,
+                      head_dim=256, block_size=16, len_range=(1, 3000))
+    f = W.make_paged_fp8(base, canary=True, k_scale=0.125, v_scale=0.25)
+    dev = PagedFP8OnDevice(f)
+    n = 4
+    rc, out, ws = dev.run(n, flags=P.PDA_DECODE_PACKED)
+    assert rc == P.PDA_OK
+    kb = W.f32_to_bf16_bits((F.decode_e4m3(f.k8) * f.k_scale).astype(np.float32))
+    vb = W.f32_to_bf16_bits((F.decode_e4m3(f.v8) * f.v_scale).astype(np.float32))
+    S, nq, D = f.num_seqs, f.num_q_heads, f.head_dim
+    po, pm, pl = A.split_partials(f.q, kb, vb, f.block_tables, f.seq_lens, f.scale, n)
+    wsn = ws.cpu().numpy().reshape(S, nq, n, D + 2).astype(np.float64)
+    assert_ml_close(wsn[..., D], pm, "packed workspace m")
+    assert_ml_close(wsn[..., D + 1], pl, "packed workspace l")
+    live = pl > 0
+    assert_out_close(wsn[..., :D][live] / wsn[..., D + 1][live][:, None],
+                     po[live] / pl[live][:, None], "packed workspace o / l")
+    assert_out_close(host_bf16(out), _ref(f), "packed fp8 split-K")
+    for nn in (1, n):
+        _, full, _ = dev.run(nn, flags=P.PDA_DECODE_PACKED)
+        for s in (0, 3, 5):
+            _, one, _ = dev.run(nn, rows=[s], flags=P.PDA_DECODE_PACKED)
+            assert np.array_equal(host_bits(one)[0], host_bits(full)[s]), (nn, s)
