@@ -55,7 +55,6 @@ constexpr float kNegInf = -__builtin_inff();
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -69,6 +68,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     v[0] = (__bf16)a;
     v[1] = (__bf16)b;
     return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two E4M3 codes (bytes 0, 1 of w, or bytes 2, 3 with HI) as a BF16 pair,
+// first code in the low half.  Exact: 3 mantissa bits, and every E4M3
+// exponent is in BF16's range; the scale operand 1.0 leaves values as they
+// are (the conversion uses only its exponent).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HI));
 }
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -198,9 +206,6 @@ __device__ __forceinline__ void seq_of_rank(const int32_t* __restrict__ lens, in
 // measured ~9 % faster than the default policy on the batch decode step).
 #ifndef PDA_FOLD_AUX
 #define PDA_FOLD_AUX 2
-#endif
-#ifndef PDA_FOLD_PV_BF16
-#define PDA_FOLD_PV_BF16 0
 #endif
 
 // Workgroups of at least this many waves merge each wave's token rows in
@@ -371,10 +376,8 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
                 // E4M3 -> FP32 -> BF16 is exact (3 mantissa bits, exponents in range)
 #pragma unroll
                 for (int w = 0; w < 2; ++w) {
-                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[w], false);
-                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)x[w], true);
-                    kr[u][2 * w] = pack_bf16x2(lo[0], lo[1]);
-                    kr[u][2 * w + 1] = pack_bf16x2(hi[0], hi[1]);
+                    kr[u][2 * w] = fp8x2_to_bf16x2<false>(x[w]);
+                    kr[u][2 * w + 1] = fp8x2_to_bf16x2<true>(x[w]);
                     vr[u][w] = y[w];
                 }
                 vr[u][2] = vr[u][3] = 0u;
@@ -467,63 +470,49 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
             }
         }
 
-#if PDA_FOLD_PV_BF16
-        if constexpr (!KV8) {
-        // P.V on token pairs: v_dot2 of (p_a, p_b) as BF16 with the two
-        // tokens' values of one dim, accumulated in FP32
-#pragma unroll
-        for (int u = 0; u < U; u += 2) {
-            uint32_t vlo[4], vhi[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                vlo[j] = __builtin_amdgcn_perm(vr[u + 1][j], vr[u][j], 0x05040100u);
-                vhi[j] = __builtin_amdgcn_perm(vr[u + 1][j], vr[u][j], 0x07060302u);
-            }
-#pragma unroll
-            for (int h = 0; h < GC; ++h) {
-                const uint32_t pp = pack_bf16x2(pa[h * U + u], pa[h * U + u + 1]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    o[h][2 * j] = dot2(pp, vlo[j], o[h][2 * j]);
-                    o[h][2 * j + 1] = dot2(pp, vhi[j], o[h][2 * j + 1]);
-                }
-            }
-        }
-        }
         if constexpr (KV8) {
-#else
-        {
-#endif
-        float vf[U][8];
+            // P.V on token pairs: the two tokens' codes of one dim are
+            // interleaved (v_perm) and decoded to a BF16 pair, then v_dot2
+            // with (p_u, p_u+1) rounded to BF16, accumulated in FP32 (fewer
+            // instructions per byte, which this half-size stream needs)
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if constexpr (KV8) {
+            for (int u = 0; u < U; u += 2) {
+                uint32_t vp[8];
 #pragma unroll
                 for (int w = 0; w < 2; ++w) {
-                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)vr[u][w], false);
-                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)vr[u][w], true);
-                    vf[u][4 * w] = lo[0];
-                    vf[u][4 * w + 1] = lo[1];
-                    vf[u][4 * w + 2] = hi[0];
-                    vf[u][4 * w + 3] = hi[1];
+                    const uint32_t x0 = __builtin_amdgcn_perm(vr[u + 1][w], vr[u][w], 0x05010400u);
+                    const uint32_t x1 = __builtin_amdgcn_perm(vr[u + 1][w], vr[u][w], 0x07030602u);
+                    vp[4 * w] = fp8x2_to_bf16x2<false>(x0);
+                    vp[4 * w + 1] = fp8x2_to_bf16x2<true>(x0);
+                    vp[4 * w + 2] = fp8x2_to_bf16x2<false>(x1);
+                    vp[4 * w + 3] = fp8x2_to_bf16x2<true>(x1);
                 }
-            } else {
+#pragma unroll
+                for (int h = 0; h < GC; ++h) {
+                    const uint32_t pp = pack_bf16x2(pa[h * U + u], pa[h * U + u + 1]);
+#pragma unroll
+                    for (int d = 0; d < 8; ++d) o[h][d] = dot2(pp, vp[d], o[h][d]);
+                }
+            }
+        } else {
+            // P.V in FP32 on the lanes holding V
+            float vf[U][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     vf[u][2 * j] = bf_lo(vr[u][j]);
                     vf[u][2 * j + 1] = bf_hi(vr[u][j]);
                 }
-            }
-        }
 #pragma unroll
-        for (int h = 0; h < GC; ++h)
+            for (int h = 0; h < GC; ++h)
 #pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                float acc = o[h][d];
+                for (int d = 0; d < 8; ++d) {
+                    float acc = o[h][d];
 #pragma unroll
-                for (int u = 0; u < U; ++u) acc = fmaf(pa[h * U + u], vf[u][d], acc);
-                o[h][d] = acc;
-            }
+                    for (int u = 0; u < U; ++u) acc = fmaf(pa[h * U + u], vf[u][d], acc);
+                    o[h][d] = acc;
+                }
         }
         wave_lds_sync();  // the next group's partials overwrite this scratch
     }

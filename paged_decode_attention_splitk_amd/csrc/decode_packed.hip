@@ -56,7 +56,6 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -68,14 +67,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // Eight E4M3 codes (w0 bytes 0..3, then w1 bytes 0..3) as eight BF16 values
-// in the same order; exact (3 mantissa bits, every exponent in range).
+// in the same order; exact (3 mantissa bits, every exponent in range; the
+// conversion's scale operand 1.0 leaves values as they are).
 __device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
-    const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
-    const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
-    const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
-    const f32x2_t d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
-    return u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(b[0], b[1]), pack_bf16x2(c[0], c[1]),
-                   pack_bf16x2(d[0], d[1])};
+    return u32x4_t{
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
 }
 
 // First of the 8 consecutive head dims that lanes of 16-lane group g hold
