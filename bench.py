@@ -153,7 +153,7 @@ def tiled_bench(args, K):
     # algorithmic bytes: valid K/V once; per active (call, sequence) its q,
     # its tile-table entries and a read + write of its (m, l, o) state; the
     # fill pass writes the state, finalize reads l, o and writes out
-    kv = int(lens.sum()) * nkv * D * kv_elem * 2
+    kv = int(lens.sum()) * nkv * D * 2 * 2
     state_slot = nq * (D + 2) * 4
     tiles_b = kv
     for tb, cnt, lbvs in calls:
