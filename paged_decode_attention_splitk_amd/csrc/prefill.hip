@@ -136,8 +136,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     // (row = idx / 32, piece = idx % 32) for K and for V
     const uint16_t* kbase = p.k + (int64_t)kvh * kD;
     const uint16_t* vbase = p.v + (int64_t)kvh * kD;
-    u32x4_t sk[kChunksPerThread], sv[kChunksPerThread];
-    auto stage_load = [&](int tile) {
+    typedef u32x4_t Stage[2][kChunksPerThread];   // K, V pieces of one tile
+    auto stage_load = [&](int tile, Stage& st) {
 #pragma unroll
         for (int i = 0; i < kChunksPerThread; ++i) {
             const int idx = tid + kThreads * i;
@@ -150,32 +150,36 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
                 if ((uint32_t)blk >= p.num_blocks) blk = 0;   // (any in-pool block)
             }
             const int64_t off = (int64_t)blk * p.blk_s + (int64_t)(j % p.bs) * p.tok_s + piece * 8;
-            sk[i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
-            sv[i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+            st[0][i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
+            st[1][i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
         }
     };
-    auto stage_store = [&](int buf) {
+    auto stage_store = [&](int buf, const Stage& st) {
         uint16_t* kt = smem + buf * 2 * kTileElems;
         uint16_t* vt = kt + kTileElems;
 #pragma unroll
         for (int i = 0; i < kChunksPerThread; ++i) {
             const int idx = tid + kThreads * i;
             const int row = idx >> 5, piece = idx & 31;
-            *reinterpret_cast<u32x4_t*>(kt + kpiece(row, piece)) = sk[i];
+            *reinterpret_cast<u32x4_t*>(kt + kpiece(row, piece)) = st[0][i];
             *reinterpret_cast<u32x4_t*>(vt + (row >> 4) * 16 * kD + vchunk(row & 15, 2 * piece)) =
-                sv[i];
+                st[1][i];
         }
     };
+    Stage ra, rb;   // tile j's pieces live in (j even ? ra : rb) from load to store
 
     if (n_tiles > 0) {
-        stage_load(0);
-        stage_store(0);
+        stage_load(0, ra);
+        stage_store(0, ra);
+        if (n_tiles > 1) stage_load(1, rb);
     }
     __syncthreads();
 
-    for (int t = 0; t < n_tiles; ++t) {
+    // tile t: loads of tile t + 2 go out (into the registers tile t held),
+    // tile t computes, tile t + 1 (loaded an iteration earlier) goes to LDS
+    auto body = [&](int t, Stage& cur, Stage& nxt) {
         const int buf = t & 1;
-        if (t + 1 < n_tiles) stage_load(t + 1);
+        if (t + 2 < n_tiles) stage_load(t + 2, cur);
         const uint16_t* kt = smem + buf * 2 * kTileElems;
         const uint16_t* vt = kt + kTileElems;
         const int key0 = t * kKT;
@@ -253,8 +257,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
                 O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, O[nb], 0, 0, 0);
             }
         }
-        if (t + 1 < n_tiles) stage_store(buf ^ 1);
+        if (t + 1 < n_tiles) stage_store(buf ^ 1, nxt);
         __syncthreads();
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+        body(t, ra, rb);
+        if (t + 1 < n_tiles) body(t + 1, rb, ra);
     }
 
     // out = O / l (0 where l is 0), rows 4g + r of this wave
