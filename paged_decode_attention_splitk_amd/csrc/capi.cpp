@@ -66,8 +66,16 @@ int head_groups(uint32_t G, int* hg) {
 // reduction order, and its output bytes, do not depend on what it is
 // batched with.  Launches that give a single sequence few workgroups get
 // wider workgroups; LDS caps the width.
+//
+// With many workgroups: 2 waves per workgroup for a BF16 cache, 1 for an FP8
+// cache (half the bytes per token: one wave per item keeps all items of the
+// batch decode shape resident at once; measured 39.4 -> 37.0 us, while BF16
+// is fastest with 2).
 #ifndef PDA_ONESHOT_WAVES_WIDE
 #define PDA_ONESHOT_WAVES_WIDE 2
+#endif
+#ifndef PDA_ONESHOT_WAVES_WIDE_FP8
+#define PDA_ONESHOT_WAVES_WIDE_FP8 1
 #endif
 
 // LDS bytes one workgroup may use on the current device (64 KiB if the
@@ -95,8 +103,10 @@ size_t lds_per_block() {
 // device's LDS per workgroup.
 bool few_items(uint32_t nkv, uint32_t nsplit) { return (uint64_t)nkv * nsplit < 128; }
 
-int oneshot_waves(uint32_t nkv, uint32_t nsplit, uint32_t head_dim, int gc) {
-    int w = few_items(nkv, nsplit) ? pda::fold_max_waves(gc) : PDA_ONESHOT_WAVES_WIDE;
+int oneshot_waves(uint32_t nkv, uint32_t nsplit, uint32_t head_dim, int gc, bool fp8) {
+    int w = few_items(nkv, nsplit)
+                ? pda::fold_max_waves(gc)
+                : (fp8 ? PDA_ONESHOT_WAVES_WIDE_FP8 : PDA_ONESHOT_WAVES_WIDE);
     const size_t cap = lds_per_block();
     while (w > 1 && pda::fold_lds_bytes((int)head_dim, gc, w) > cap) --w;
     return w;
@@ -218,7 +228,7 @@ int run_partials(const DecodeShape& s, const void* q, const void* k, const void*
     pda::FoldParams p = fold_params(s, q, k, v, bt, lens, hg, sc, nsplit);
     p.ws = ws;
     p.v_scale = kv.v_scale;
-    const int waves = oneshot_waves(s.nkv, nsplit, s.D, gc);
+    const int waves = oneshot_waves(s.nkv, nsplit, s.D, gc, kv.fp8);
     const uint64_t gx = (uint64_t)s.nkv * hg * nsplit;
     hipError_t e = pda::launch_fold(pda::kModePartial, (int)s.D, gc, p, (uint32_t)gx, s.num_seqs,
                                     waves, stream, kv.fp8);
@@ -295,7 +305,7 @@ int decode_impl(const DecodeShape& s, const void* q, const void* k, const void* 
         pda::FoldParams p = fold_params(s, q, k, v, bt, lens, hg, sc, 1);
         p.out = static_cast<uint16_t*>(out);
         p.v_scale = kv.v_scale;
-        const int waves = oneshot_waves(s.nkv, 1, s.D, gc);
+        const int waves = oneshot_waves(s.nkv, 1, s.D, gc, kv.fp8);
         hipError_t e = pda::launch_fold(pda::kModeFinal, (int)s.D, gc, p, s.nkv * (uint32_t)hg,
                                         s.num_seqs, waves, st, kv.fp8);
         if (e != hipSuccess) return hip_fail(e, "single-split decode launch");
