@@ -61,8 +61,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     bf16x2_t v;
     v[0] = (__bf16)a;
@@ -495,24 +493,27 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
                 }
             }
         } else {
-            // P.V in FP32 on the lanes holding V
-            float vf[U][8];
+            // P.V on token pairs: (p_u, p_u+1) rounded to BF16 (as the MFMA
+            // kernels do) against the two tokens' values of one dim, v_dot2,
+            // accumulated in FP32: half the instructions of FP32 FMAs
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+            for (int u = 0; u < U; u += 2) {
+                uint32_t vlo[4], vhi[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    vf[u][2 * j] = bf_lo(vr[u][j]);
-                    vf[u][2 * j + 1] = bf_hi(vr[u][j]);
+                    vlo[j] = __builtin_amdgcn_perm(vr[u + 1][j], vr[u][j], 0x05040100u);
+                    vhi[j] = __builtin_amdgcn_perm(vr[u + 1][j], vr[u][j], 0x07060302u);
                 }
 #pragma unroll
-            for (int h = 0; h < GC; ++h)
+                for (int h = 0; h < GC; ++h) {
+                    const uint32_t pp = pack_bf16x2(pa[h * U + u], pa[h * U + u + 1]);
 #pragma unroll
-                for (int d = 0; d < 8; ++d) {
-                    float acc = o[h][d];
-#pragma unroll
-                    for (int u = 0; u < U; ++u) acc = fmaf(pa[h * U + u], vf[u][d], acc);
-                    o[h][d] = acc;
+                    for (int j = 0; j < 4; ++j) {
+                        o[h][2 * j] = dot2(pp, vlo[j], o[h][2 * j]);
+                        o[h][2 * j + 1] = dot2(pp, vhi[j], o[h][2 * j + 1]);
+                    }
                 }
+            }
         }
         wave_lds_sync();  // the next group's partials overwrite this scratch
     }
