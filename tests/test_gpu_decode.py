@@ -140,6 +140,51 @@ def test_other_shapes(D, nq, nkv):
         assert_out_close(host_bf16(out), ref, f"splits={n}")
 
 
+@pytest.mark.parametrize("bs,D", [(64, 128), (128, 64), (48, 256)])
+def test_larger_blocks(bs, D):
+    """Block sizes past one group of tokens (several groups per block, and a
+    non-power-of-two block), with ragged tails, at 1, 7 and 16 splits."""
+    say(f"[blocks] bs={bs} D={D}")
+    lens = (1, bs - 1, bs, bs + 1, 5 * bs + 3, 2000)
+    base = W.Workload(name="blocks", seed=15, num_seqs=len(lens), num_q_heads=8, num_kv_heads=2,
+                      head_dim=D, block_size=bs, seq_lens=lens)
+    inp = W.make_paged(base, canary=True)
+    dev = PagedOnDevice(inp)
+    ref, _, _ = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
+                               inp.scale)
+    for n in (1, 7, 16):
+        rc, out, ws = dev.run(n)
+        assert rc == P.PDA_OK
+        assert_out_close(host_bf16(out), ref, f"bs={bs} splits={n}")
+        if n > 1:
+            _check_partials(dev, ws, n)
+
+
+def test_many_sequences_maximum_splits():
+    """A large batch (600 sequences: the unranked schedule past 64) of short
+    and empty sequences at the split ceiling, sampled rows against the
+    oracle, and every output row alone vs co-batched for a sample."""
+    base = W.Workload(name="many", seed=16, num_seqs=600, num_q_heads=16, num_kv_heads=2,
+                      head_dim=128, block_size=16, len_range=(0, 300))
+    inp = W.make_paged(base, canary=True)
+    dev = PagedOnDevice(inp)
+    n = P.pda_max_decode_splits()
+    say(f"[many] seqs=600 splits={n}")
+    rc, out, _ = dev.run(n)
+    assert rc == P.PDA_OK
+    rows = [0, 1, 63, 64, 65, 299, 598, 599]
+    sub = W.subset_paged(inp, rows)
+    ref, _, _ = A.paged_decode(sub.q, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens,
+                               sub.scale)
+    assert_out_close(host_bf16(out)[rows], ref, "many")
+    full = host_bits(out)
+    for s in rows:
+        _, one, _ = dev.run(n, rows=[s])
+        assert np.array_equal(host_bits(one)[0], full[s]), f"seq {s} differs alone"
+    empty = np.flatnonzero(inp.seq_lens == 0)
+    assert np.all(full[empty] == 0)
+
+
 def test_batch_invariance_auto_and_pinned():
     """Each sequence's output bytes are the same alone and co-batched with
     127 others, under Auto and Pinned split counts."""
