@@ -253,3 +253,22 @@ def test_decode_fp8_packed_not_applicable_and_empty():
             P.pda_splitk_partials_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 10**9, 2, 8, 2, 128, 16,
                                       8, 32, 0.1, bad.get("ks", 0.01), 0.02, bad.get("n", 2), 0,
                                       0)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without libpda.so the binding refuses to import (no CPU fallback)."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "paged_decode_attention_splitk_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(P.__file__), "__init__.py"), pkg / "__init__.py")
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "try:\n"
+            "    import paged_decode_attention_splitk_amd\n"
+            "except ImportError as e:\n"
+            "    print('refused:', e); sys.exit(0)\n"
+            "sys.exit(1)\n") % str(tmp_path)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "no CPU fallback" in r.stdout
