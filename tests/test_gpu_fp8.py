@@ -211,3 +211,43 @@ def test_packed_fp8_partials_and_invariance():
         for s in (0, 3, 5):
             _, one, _ = dev.run(nn, rows=[s], flags=P.PDA_DECODE_PACKED)
             assert np.array_equal(host_bits(one)[0], host_bits(full)[s]), (nn, s)
+
+
+_DEFAULT_CHILD_FP8 = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np, torch
+import paged_decode_attention_splitk_amd as P
+import workloads as W
+from tests.gpu_util import PagedFP8OnDevice, host_bits
+assert P.pda_gqa_pack_enabled()
+base = W.Workload(name="pdef8", seed=23, num_seqs=3, num_q_heads=16, num_kv_heads=2,
+                  head_dim=256, block_size=16, seq_lens=(5, 300, 1000))
+dev = PagedFP8OnDevice(W.make_paged_fp8(base, canary=True))
+_, d, _ = dev.run(1, flags=P.PDA_DECODE_DEFAULT)
+_, pk, _ = dev.run(1, flags=P.PDA_DECODE_PACKED)
+_, up, _ = dev.run(1)
+assert np.array_equal(host_bits(d), host_bits(pk))
+assert not np.array_equal(host_bits(pk), host_bits(up))
+# split launches stay unpacked under the default
+_, d4, _ = dev.run(4, flags=P.PDA_DECODE_DEFAULT)
+_, u4, _ = dev.run(4)
+assert np.array_equal(host_bits(d4), host_bits(u4))
+print("fp8 default->packed ok", flush=True)
+"""
+
+
+def test_default_flag_with_pack_switched_on_in_env():
+    """With the pack switch on in the environment, the FP8 default dispatch
+    takes the packed kernel on non-split launches of the packed shape only,
+    as for BF16 caches."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, METRALE_ATTN_DECODE_GQA_PACK="on")
+    say("[fp8 default flag, pack on] child process")
+    r = subprocess.run([sys.executable, "-c", _DEFAULT_CHILD_FP8, root], env=env, cwd=root,
+                       capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert "fp8 default->packed ok" in r.stdout
