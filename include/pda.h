@@ -285,6 +285,14 @@ int pda_device_cu_count(int device, uint32_t* cu_count);
  * head_dim in {64, 128, 256}, block_size a positive multiple of 16, q /
  * caches / out 16-byte aligned, workspace 8-byte aligned.  num_seqs == 0
  * launches nothing.
+ *
+ * Launches with fewer than 128 (KV head, split) pairs per sequence (a long
+ * single sequence, small split counts) split each split over several
+ * workgroups that hand partial results to each other through a device
+ * array the library owns (16 MiB of records and 64 Ki counters per GPU, no
+ * allocation; batches beyond it run as several launches).  Such calls
+ * (this one, pda_splitk_partials and their FP8 forms) must not overlap on
+ * one GPU: issue them on one stream, or order the streams.
  * ------------------------------------------------------------------------ */
 int pda_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, const int32_t* seq_lens, void* out,

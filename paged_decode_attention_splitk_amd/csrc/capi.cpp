@@ -112,15 +112,74 @@ int oneshot_waves(uint32_t nkv, uint32_t nsplit, uint32_t head_dim, int gc, bool
     return w;
 }
 
-int tiled_waves(uint32_t head_dim, int gc) {
-    int w = 8;
-    while (w > 1 && pda::fold_lds_bytes((int)head_dim, gc, w) > 64 * 1024) --w;
-    return w;
-}
-
 struct DecodeShape {
     uint32_t num_seqs, nq, nkv, D, bs, max_blocks, num_blocks;
 };
+
+// Parts per item of a one-shot launch (workgroups that share one split of
+// one sequence and head group, the last to finish combining them).  Like the
+// wave count, a pure function of the shape and the split count: launches
+// that give a sequence few (KV head, split) items split each item so that a
+// single sequence still offers about PDA_PART_TARGET workgroups (the CU count
+// of an MI355X), within kMaxParts and the library's part arrays.
+#ifndef PDA_PART_TARGET
+#define PDA_PART_TARGET 256
+#endif
+int oneshot_parts(uint32_t nkv, uint32_t hg, uint32_t nsplit, int gc, uint32_t head_dim) {
+    if (!few_items(nkv, nsplit)) return 1;
+    const uint64_t items = (uint64_t)nkv * hg * nsplit;   // per sequence
+    uint64_t parts = (PDA_PART_TARGET + items - 1) / items;
+    if (parts > (uint64_t)pda::kMaxParts) parts = pda::kMaxParts;
+    while (parts > 1 && (items * parts * pda::part_rec_floats(gc, (int)head_dim) >
+                             pda::kPartSubFloats ||
+                         items > pda::kPartTickets))
+        --parts;
+    return (int)parts;
+}
+
+// Sequences per launch that the library's part arrays hold at `parts`.
+uint32_t part_rows(uint64_t items_per_row, int parts, int gc, uint32_t head_dim) {
+    const uint64_t by_tick = pda::kPartTickets / items_per_row;
+    const uint64_t by_sub =
+        pda::kPartSubFloats / (items_per_row * parts * pda::part_rec_floats(gc, (int)head_dim));
+    const uint64_t r = by_tick < by_sub ? by_tick : by_sub;
+    return r > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)r;
+}
+
+// Launches a one-shot fold over all sequences; with parts, in runs of
+// sequences that fit the library's part arrays (each run is an ordinary
+// launch over fewer rows: a sequence's arithmetic does not change).
+hipError_t launch_oneshot(int mode, const DecodeShape& s, int gc, int hg, pda::FoldParams p,
+                          uint32_t nsplit, int waves, hipStream_t stream, bool kv8) {
+    const int parts = oneshot_parts(s.nkv, (uint32_t)hg, nsplit, gc, s.D);
+    const uint64_t items = (uint64_t)s.nkv * hg * nsplit;
+    p.parts = parts;
+    p.sub = nullptr;
+    p.tick = nullptr;
+    const uint32_t gx = (uint32_t)(items * parts);
+    const uint32_t chunk = parts > 1 ? part_rows(items, parts, gc, s.D) : s.num_seqs;
+    for (uint32_t r0 = 0; r0 < s.num_seqs; r0 += chunk) {
+        const uint32_t rows = s.num_seqs - r0 < chunk ? s.num_seqs - r0 : chunk;
+        pda::FoldParams c = p;
+        c.q = p.q + (uint64_t)r0 * s.nq * s.D;
+        c.tables = p.tables + (uint64_t)r0 * s.max_blocks;
+        c.lens = p.lens + r0;
+        if (p.ws) c.ws = p.ws + (uint64_t)r0 * s.nq * nsplit * (s.D + 2);
+        if (p.out) c.out = p.out + (uint64_t)r0 * s.nq * s.D;
+        hipError_t e = pda::launch_fold(mode, (int)s.D, gc, c, gx, rows, waves, stream, kv8);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+#ifndef PDA_TILED_WAVES
+#define PDA_TILED_WAVES 8
+#endif
+int tiled_waves(uint32_t head_dim, int gc) {
+    int w = PDA_TILED_WAVES;
+    while (w > 1 && pda::fold_lds_bytes((int)head_dim, gc, w) > 64 * 1024) --w;
+    return w;
+}
 
 int check_decode(const DecodeShape& s, const void* q, const void* k, const void* v,
                  const int32_t* bt, const int32_t* lens, const void* out, bool need_out) {
@@ -171,6 +230,7 @@ pda::FoldParams fold_params(const DecodeShape& s, const void* q, const void* k, 
     p.table_stride = (int)s.max_blocks;
     p.nsplit = (int)nsplit;
     p.c = scale * kLog2e;
+    p.parts = 1;
     return p;
 }
 
@@ -229,9 +289,8 @@ int run_partials(const DecodeShape& s, const void* q, const void* k, const void*
     p.ws = ws;
     p.v_scale = kv.v_scale;
     const int waves = oneshot_waves(s.nkv, nsplit, s.D, gc, kv.fp8);
-    const uint64_t gx = (uint64_t)s.nkv * hg * nsplit;
-    hipError_t e = pda::launch_fold(pda::kModePartial, (int)s.D, gc, p, (uint32_t)gx, s.num_seqs,
-                                    waves, stream, kv.fp8);
+    hipError_t e =
+        launch_oneshot(pda::kModePartial, s, gc, hg, p, nsplit, waves, stream, kv.fp8);
     if (e != hipSuccess) return hip_fail(e, "split-K partial launch");
     return PDA_OK;
 }
@@ -306,8 +365,7 @@ int decode_impl(const DecodeShape& s, const void* q, const void* k, const void* 
         p.out = static_cast<uint16_t*>(out);
         p.v_scale = kv.v_scale;
         const int waves = oneshot_waves(s.nkv, 1, s.D, gc, kv.fp8);
-        hipError_t e = pda::launch_fold(pda::kModeFinal, (int)s.D, gc, p, s.nkv * (uint32_t)hg,
-                                        s.num_seqs, waves, st, kv.fp8);
+        hipError_t e = launch_oneshot(pda::kModeFinal, s, gc, hg, p, 1, waves, st, kv.fp8);
         if (e != hipSuccess) return hip_fail(e, "single-split decode launch");
         return ok();
     }
@@ -611,6 +669,7 @@ int pda_tiled_step_tile(pda_tiled* t, const void* q, const void* k_pool, const v
     p.lbvs = last_block_valid_slots;
     // the step takes no scale: 1 / sqrt(head_dim), rounded once to FP32
     p.c = (float)(1.0 / std::sqrt((double)d.head_dim)) * kLog2e;
+    p.parts = 1;
     const int waves = tiled_waves(d.head_dim, gc);
     hipError_t e = pda::launch_fold(pda::kModeTiled, (int)d.head_dim, gc, p,
                                     (uint32_t)(d.num_kv_heads * hg), num_seqs, waves,

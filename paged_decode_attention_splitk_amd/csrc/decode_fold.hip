@@ -78,6 +78,19 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 }
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Part records are written and read at device scope (stores that write
+// through to the level every XCD shares, loads that do not hit a stale
+// copy), so handing them over needs no L2 writeback or invalidate: a writer
+// waits for its record stores to complete before its workgroup takes a
+// ticket, and the combining workgroup loads the records only after taking
+// the last ticket.
+__device__ __forceinline__ void put_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_dev(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(
@@ -210,6 +223,13 @@ __device__ __forceinline__ void seq_of_rank(const int32_t* __restrict__ lens, in
 // registers before the LDS merge (see the epilogue).
 constexpr int kRowMergeWaves = 4;
 
+// The library's own part records and arrival tickets, for launches that
+// split an item over several workgroups without a handle of their own.
+// Tickets start at 0 (zero-initialised) and the combining workgroup puts
+// its ticket back to 0, so every launch finds them at 0.
+__device__ __align__(256) float g_part_sub[kPartSubFloats];
+__device__ __align__(256) uint32_t g_part_tick[kPartTickets];
+
 // Lane layout of the fold for head_dim D and GC heads per workgroup.
 template <int D, int GC>
 struct FoldShape {
@@ -232,7 +252,9 @@ struct FoldShape {
 // per SIMD fit their registers), 8 beyond.
 __host__ __device__ constexpr int fold_max_threads(int gc) { return gc <= 6 ? 768 : 512; }
 
-template <int MODE, int D, int GC, bool KV8>
+// PARTS: the item may be split over p.parts workgroups (one-shot modes);
+// without it the kernel has no part code at all.
+template <int MODE, int D, int GC, bool KV8, bool PARTS>
 __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldParams p) {
     using S = FoldShape<D, GC>;
     constexpr int LPT = S::LPT, ROWS = S::ROWS, U = S::U, TG = S::TG, NP = S::NP,
@@ -248,8 +270,12 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
     seq_of_rank(p.lens, (int)gridDim.y, (int)blockIdx.y,
                 MODE == kModeTiled ? p.table_stride : p.table_stride * p.bs, seq, slen);
     const int per_seq = p.nkv * p.HG;
-    const int kvhg = MODE == kModeTiled ? (int)blockIdx.x : (int)blockIdx.x % per_seq;
-    const int split = MODE == kModeTiled ? 0 : (int)blockIdx.x / per_seq;
+    static_assert(!(PARTS && MODE == kModeTiled), "tiled launches take no parts");
+    const int P = PARTS ? p.parts : 1;            // workgroups per item
+    const int bx = (int)blockIdx.x / P;           // the item's index in the row
+    const int part = (int)blockIdx.x - bx * P;
+    const int kvhg = MODE == kModeTiled ? bx : bx % per_seq;
+    const int split = MODE == kModeTiled ? 0 : bx / per_seq;
     const int kvh = kvhg / p.HG, hg = kvhg % p.HG;
     const int h0 = kvh * p.G + hg * GC;                 // first q head of the group
     const int gcount = min(GC, p.G - hg * GC);          // heads this group carries
@@ -269,7 +295,9 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
         t_end = (int64_t)t_begin + chunk < L ? t_begin + chunk : L;
         if (t_begin >= t_end) {
             // nothing to fold: an empty split leaves m = -inf, l = 0 (its o is
-            // never read); a single empty split is an all-zero output
+            // never read); a single empty split is an all-zero output.  Every
+            // part sees the same empty item, so none takes a ticket.
+            if (part != 0) return;
             const int64_t row_q0 = (int64_t)seq * p.nq + h0;
             if constexpr (MODE == kModePartial) {
                 if (tid < gcount) {
@@ -327,8 +355,21 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
     const uint32_t voff0 = (uint32_t)(sub * 8 * EB);           // the group's first token
     const uint32_t rec = (uint32_t)((p.bs - 1) * tok_b + D * EB);  // bytes a block spans
 
+    // This workgroup's run of the item: with parts, part i folds blocks
+    // [i * per, (i + 1) * per) of the item (per = ceil(blocks / parts)),
+    // possibly none.
+    if (P > 1) {
+        const int nb_item = (t_end - t_begin + p.bs - 1) / p.bs;
+        const int per = (nb_item + P - 1) / P;
+        const int64_t fb = (int64_t)t_begin + (int64_t)part * per * p.bs;
+        const int f_begin = fb < t_end ? (int)fb : t_end;
+        t_end = (int64_t)f_begin + (int64_t)per * p.bs < t_end ? f_begin + per * p.bs : t_end;
+        t_begin = f_begin;
+    }
+
     // a live range starts on a block (hence group) boundary; an empty split
-    // starts at the sequence end, which need not be aligned: it folds nothing
+    // or part starts at the range end, which need not be aligned: it folds
+    // nothing
     const int gpb = p.bs / TG;  // groups per block
     const int g_first = t_begin / TG;
     const int g_end = t_end > t_begin ? (t_end + TG - 1) / TG : g_first;
@@ -527,7 +568,8 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
 
     // Wave epilogue, then every contributor's state goes to LDS and one
     // fixed-order pass merges them.  Layout (aliasing the loop scratch):
-    // o [NC][GC][D], m [NC][GC], l [NC][GC], weights [NC + 1][GC], L [GC].
+    // o [NC][GC][D], m [NC][GC], l [NC][GC], weights [max(NC, kMaxParts) +
+    // 1][GC], L [GC], ticket.
     //  * nw < kRowMergeWaves: each (wave, row) state is a contributor,
     //    NC = nw * ROWS (cheapest for few waves).
     //  * otherwise the wave's ROWS row states merge first, with cross-lane
@@ -542,7 +584,7 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
     float* em = eo + NC * GC * D;
     float* el = em + NC * GC;
     float* ew = el + NC * GC;
-    float* eL = ew + (NC + 1) * GC;
+    float* eL = ew + ((NC > kMaxParts ? NC : kMaxParts) + 1) * GC;
     if (row_merge) {
         float wM[GC], wL[GC];   // per head, identical in every lane of the wave
 #pragma unroll
@@ -596,12 +638,19 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
     }
     __syncthreads();
 
-    // Per head: the workgroup max, every contributor's weight, and l.
+    // Per head: the workgroup max, every contributor's weight, and l (and
+    // the running state of a tiled launch, which never has parts).
+    constexpr bool with_old = MODE == kModeTiled;
     const int64_t row_q = (int64_t)seq * p.nq + h0;  // first q slot of the group
+    // this part's record: o [GC][D], m [GC] (log2 units), l [GC]
+    const int64_t item = (int64_t)blockIdx.y * (gridDim.x / P) + bx;
+    constexpr int REC = (int)part_rec_floats(GC, D);
+    float* const psub = p.sub ? p.sub : g_part_sub;
+    float* const prec = psub + (item * P + part) * REC;
     if (tid < gcount) {
         const int h = tid;
         float M = kNegInf, m_old = kNegInf, m2_old = kNegInf, l_old = 0.f;
-        if constexpr (MODE == kModeTiled) {
+        if (with_old) {
             m_old = p.ws[row_q + h];
             l_old = p.l_state[row_q + h];
             m2_old = m_old * kLog2e;
@@ -610,7 +659,7 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
         for (int c = 0; c < NC; ++c) M = fmaxf(M, em[c * GC + h]);
         const float Ms = M == kNegInf ? 0.f : M;
         float L = 0.f;
-        if constexpr (MODE == kModeTiled) {
+        if (with_old) {
             const float wo = fexp2(m2_old - Ms);
             ew[NC * GC + h] = wo;
             L = wo * l_old;
@@ -636,15 +685,20 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
             }
         }
         eL[h] = L;
-        const float m_nat = M * kLn2;
-        if constexpr (MODE == kModePartial) {
-            float* slot = p.ws + ((row_q + h) * p.nsplit + split) * (int64_t)(D + 2);
-            slot[D] = m_nat;
-            slot[D + 1] = L;
-        } else if constexpr (MODE == kModeTiled) {
-            // keep the stored max bit-identical when this tile did not raise it
-            p.ws[row_q + h] = M == m2_old ? m_old : m_nat;
-            p.l_state[row_q + h] = L;
+        if (P > 1) {
+            put_dev(prec + GC * D + h, M);
+            put_dev(prec + GC * D + GC + h, L);
+        } else {
+            const float m_nat = M * kLn2;
+            if constexpr (MODE == kModePartial) {
+                float* slot = p.ws + ((row_q + h) * p.nsplit + split) * (int64_t)(D + 2);
+                slot[D] = m_nat;
+                slot[D + 1] = L;
+            } else if constexpr (MODE == kModeTiled) {
+                // keep the stored max bit-identical when this tile did not raise it
+                p.ws[row_q + h] = M == m2_old ? m_old : m_nat;
+                p.l_state[row_q + h] = L;
+            }
         }
     }
     __syncthreads();
@@ -656,7 +710,7 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
         const int d = (i - h * (D / 2)) * 2;
         float o0 = 0.f, o1 = 0.f;
         const int64_t qs = row_q + h;
-        if constexpr (MODE == kModeTiled) {
+        if (with_old) {
             const float2 prev = *reinterpret_cast<const float2*>(p.o_state + qs * D + d);
             const float wo = ew[NC * GC + h];
             o0 = wo * prev.x;
@@ -669,7 +723,10 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
             o1 += wt * x.y;
         }
         const float L = eL[h];
-        if constexpr (MODE == kModePartial) {
+        if (P > 1) {
+            put_dev(prec + h * D + d, o0);
+            put_dev(prec + h * D + d + 1, o1);
+        } else if constexpr (MODE == kModePartial) {
             if (L > 0.f) {
                 float* slot = p.ws + (qs * p.nsplit + split) * (int64_t)(D + 2);
                 *reinterpret_cast<float2*>(slot + d) = make_float2(o0, o1);
@@ -679,6 +736,81 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
             *reinterpret_cast<uint32_t*>(p.out + qs * D + d) = v;
         } else {
             *reinterpret_cast<float2*>(p.o_state + qs * D + d) = make_float2(o0, o1);
+        }
+    }
+    if (P == 1) return;
+
+    // Parts: publish this record, take a ticket; the last part to arrive
+    // combines every part's record, in part order, with the same weighting,
+    // so the result depends on the item's data and the part count only,
+    // never on arrival order.
+    if constexpr (PARTS) {
+        uint32_t* const tick = (p.tick ? p.tick : g_part_tick) + item;
+        uint32_t* const eT = reinterpret_cast<uint32_t*>(eL + GC);
+        __builtin_amdgcn_s_waitcnt(0);   // this thread's record stores are complete
+        __syncthreads();
+        if (tid == 0)
+            *eT = __hip_atomic_fetch_add(tick, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (*eT != (uint32_t)(P - 1)) return;
+        if (tid == 0) __hip_atomic_store(tick, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float* const recs = psub + item * P * REC;
+        // weights: ew[i * GC + h] for part i
+        if (tid < gcount) {
+            const int h = tid;
+            float M = kNegInf;
+            float mv[kMaxParts], lv[kMaxParts];
+#pragma unroll
+            for (int i = 0; i < kMaxParts; ++i) {
+                const int ii = i < P ? i : P - 1;
+                mv[i] = get_dev(recs + ii * REC + GC * D + h);
+                lv[i] = get_dev(recs + ii * REC + GC * D + GC + h);
+            }
+#pragma unroll
+            for (int i = 0; i < kMaxParts; ++i)
+                if (i < P && lv[i] > 0.f) M = fmaxf(M, mv[i]);
+            const float Ms = M == kNegInf ? 0.f : M;
+            float L = 0.f;
+#pragma unroll
+            for (int i = 0; i < kMaxParts; ++i) {
+                if (i < P) {
+                    // a part that folded nothing has l = 0 and takes no weight
+                    const float wt = lv[i] > 0.f ? fexp2(mv[i] - Ms) : 0.f;
+                    ew[i * GC + h] = wt;
+                    L += wt * lv[i];
+                }
+            }
+            eL[h] = L;
+            if constexpr (MODE == kModePartial) {
+                float* slot = p.ws + ((row_q + h) * p.nsplit + split) * (int64_t)(D + 2);
+                slot[D] = M * kLn2;
+                slot[D + 1] = L;
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < nitems; i += blockDim.x) {
+            const int h = i / (D / 2);
+            const int d = (i - h * (D / 2)) * 2;
+            float o0 = 0.f, o1 = 0.f;
+            const int64_t qs = row_q + h;
+            for (int c = 0; c < P; ++c) {
+                const float wt = ew[c * GC + h];
+                if (wt != 0.f) {   // an empty part's o is never read
+                    const float* x = recs + c * REC + h * D + d;
+                    o0 += wt * get_dev(x);
+                    o1 += wt * get_dev(x + 1);
+                }
+            }
+            const float L = eL[h];
+            if constexpr (MODE == kModePartial) {
+                if (L > 0.f) {
+                    float* slot = p.ws + (qs * p.nsplit + split) * (int64_t)(D + 2);
+                    *reinterpret_cast<float2*>(slot + d) = make_float2(o0, o1);
+                }
+            } else {
+                const uint32_t v = L > 0.f ? pack_bf16x2(o0 / L, o1 / L) : 0u;
+                *reinterpret_cast<uint32_t*>(p.out + qs * D + d) = v;
+            }
         }
     }
 }
@@ -777,36 +909,46 @@ __global__ __launch_bounds__(256) void tiled_finalize_kernel(const float* __rest
 
 using FoldFn = void (*)(FoldParams);
 
-template <int MODE, int D, bool KV8>
+template <int MODE, int D, bool KV8, bool PARTS>
 FoldFn pick_gc(int gc) {
     switch (gc) {
-        case 1: return fold_kernel<MODE, D, 1, KV8>;
-        case 2: return fold_kernel<MODE, D, 2, KV8>;
-        case 3: return fold_kernel<MODE, D, 3, KV8>;
-        case 4: return fold_kernel<MODE, D, 4, KV8>;
-        case 5: return fold_kernel<MODE, D, 5, KV8>;
-        case 6: return fold_kernel<MODE, D, 6, KV8>;
-        case 7: return fold_kernel<MODE, D, 7, KV8>;
-        case 8: return fold_kernel<MODE, D, 8, KV8>;
+        case 1: return fold_kernel<MODE, D, 1, KV8, PARTS>;
+        case 2: return fold_kernel<MODE, D, 2, KV8, PARTS>;
+        case 3: return fold_kernel<MODE, D, 3, KV8, PARTS>;
+        case 4: return fold_kernel<MODE, D, 4, KV8, PARTS>;
+        case 5: return fold_kernel<MODE, D, 5, KV8, PARTS>;
+        case 6: return fold_kernel<MODE, D, 6, KV8, PARTS>;
+        case 7: return fold_kernel<MODE, D, 7, KV8, PARTS>;
+        case 8: return fold_kernel<MODE, D, 8, KV8, PARTS>;
         default: return nullptr;
     }
 }
 
-template <int MODE, bool KV8>
+template <int MODE, bool KV8, bool PARTS = false>
 FoldFn pick_d(int D, int gc) {
     switch (D) {
-        case 64: return pick_gc<MODE, 64, KV8>(gc);
-        case 128: return pick_gc<MODE, 128, KV8>(gc);
-        case 256: return pick_gc<MODE, 256, KV8>(gc);
+        case 64: return pick_gc<MODE, 64, KV8, PARTS>(gc);
+        case 128: return pick_gc<MODE, 128, KV8, PARTS>(gc);
+        case 256: return pick_gc<MODE, 256, KV8, PARTS>(gc);
         default: return nullptr;
     }
+}
+
+// One-shot modes, with or without parts.
+template <int MODE>
+FoldFn pick_oneshot(int D, int gc, bool kv8, bool parts) {
+    if (parts) return kv8 ? pick_d<MODE, true, true>(D, gc) : pick_d<MODE, false, true>(D, gc);
+    return kv8 ? pick_d<MODE, true>(D, gc) : pick_d<MODE, false>(D, gc);
 }
 
 template <int D, int GC>
 size_t fold_lds_floats(int waves) {
     using S = FoldShape<D, GC>;
     const size_t nc = (size_t)(waves >= kRowMergeWaves ? waves : waves * S::ROWS);
-    const size_t epi = nc * GC * D + 2 * nc * GC + (nc + 1) * GC + GC;
+    // o, m, l per contributor; weights for max(contributors, parts) + 1;
+    // L per head; the ticket word
+    const size_t nw8 = nc > (size_t)kMaxParts ? nc : (size_t)kMaxParts;
+    const size_t epi = nc * GC * D + 2 * nc * GC + (nw8 + 1) * GC + GC + 1;
     const size_t loop = (size_t)waves * S::WAVE_FLOATS;
     return epi > loop ? epi : loop;
 }
@@ -842,17 +984,17 @@ size_t fold_lds_bytes(int head_dim, int gc, int waves) {
 hipError_t launch_fold(int mode, int head_dim, int gc, const FoldParams& p, uint32_t grid_x,
                        uint32_t grid_y, int waves, hipStream_t stream, bool kv8) {
     FoldFn fn = nullptr;
+    const bool parts = p.parts > 1;
     switch (mode) {
-        case kModePartial:
-            fn = kv8 ? pick_d<kModePartial, true>(head_dim, gc) : pick_d<kModePartial, false>(head_dim, gc);
-            break;
-        case kModeFinal:
-            fn = kv8 ? pick_d<kModeFinal, true>(head_dim, gc) : pick_d<kModeFinal, false>(head_dim, gc);
-            break;
+        case kModePartial: fn = pick_oneshot<kModePartial>(head_dim, gc, kv8, parts); break;
+        case kModeFinal: fn = pick_oneshot<kModeFinal>(head_dim, gc, kv8, parts); break;
         case kModeTiled: fn = kv8 ? nullptr : pick_d<kModeTiled, false>(head_dim, gc); break;
         default: break;
     }
     if (!fn || waves < 1 || 64 * waves > fold_max_threads(gc)) return hipErrorInvalidValue;
+    if (p.parts < 1 || p.parts > kMaxParts || grid_x % (uint32_t)p.parts != 0 ||
+        (mode == kModeTiled && p.parts != 1))
+        return hipErrorInvalidValue;
     const size_t lds = fold_lds_bytes(head_dim, gc, waves);
     if (lds > 64 * 1024) {
         // dynamic LDS past 64 KiB is requested per kernel, once

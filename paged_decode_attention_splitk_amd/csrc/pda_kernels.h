@@ -33,10 +33,30 @@ struct FoldParams {
     int lbvs;                // valid slots of a tile's last block (tiled)
     float c;                 // scale * log2(e) (times k_scale for an FP8 cache)
     float v_scale;           // FP8 cache only: V = decode(v8) * v_scale
+    // Parts (one-shot launches only): `parts` workgroups share one item (one
+    // split of one sequence and head group), each folding a contiguous run
+    // of its blocks into a record of `sub`; the last to arrive (ticket in
+    // `tick`) combines the records in part order and writes what one
+    // workgroup would.  parts == 1: no records, no tickets.  Null sub /
+    // tick: the library's own device arrays (kPartSubFloats / kPartTickets
+    // entries).
+    int parts;
+    float* sub;              // [item][part] records (part_rec_floats each)
+    uint32_t* tick;          // [item] arrival counters, 0 between launches
 };
 
 // Heads one fold workgroup carries at most (the packed width).
 constexpr int kMaxHeadsPerGroup = 8;
+
+// Most parts per item, and the capacity of the library's own part arrays.
+constexpr int kMaxParts = 8;
+constexpr uint64_t kPartTickets = 1u << 16;
+constexpr uint64_t kPartSubFloats = 1u << 22;   // 16 MiB
+// Floats of one part record for gc heads of head_dim d: o [gc][d], m [gc],
+// l [gc], padded to whole 128-byte lines so that no two records share one.
+constexpr uint64_t part_rec_floats(int gc, int d) {
+    return ((uint64_t)gc * (d + 2) + 31) / 32 * 32;
+}
 
 // LDS bytes a fold workgroup of `waves` waves needs.
 size_t fold_lds_bytes(int head_dim, int gc, int waves);

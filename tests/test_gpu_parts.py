@@ -1,0 +1,117 @@
+"""GPU parity of the fold kernel's parts form: one-shot launches that give a
+sequence few (KV head, split) items split each item over several
+workgroups, whose last one to finish combines their records.  Checked
+against the FP64 oracle, for batch invariance (a sequence's bytes alone and
+co-batched, also across runs of sequences that the library launches
+separately), and for repeatability (the arrival tickets are back at zero
+after every launch).  Tiled launches, which never take parts, are checked
+at several tile capacities.  Needs an MI355X."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+import workloads as W
+from oracle import attention as A
+from tests.gpu_util import (PagedOnDevice, ScratchOnDevice, assert_ml_close, assert_out_close,
+                            host_bf16, host_bits, say)
+
+import paged_decode_attention_splitk_amd as P
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _partials_close(inp, ws, n):
+    S, nq, D = inp.num_seqs, inp.num_q_heads, inp.head_dim
+    w = ws.cpu().numpy().reshape(S, nq, n, D + 2).astype(np.float64)
+    po, pm, pl = A.split_partials(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                                  inp.seq_lens, inp.scale, n)
+    assert_ml_close(w[..., D], pm, "workspace m")
+    assert_ml_close(w[..., D + 1], pl, "workspace l")
+    live = pl > 0
+    assert_out_close(w[..., :D][live] / w[..., D + 1][live][:, None],
+                     po[live] / pl[live][:, None], "workspace o / l")
+
+
+# 24 q / 4 kv heads at D 128 (the long-sequence shape): at 16 splits a
+# sequence has 64 items, so each is split over 4 workgroups; at 1 and 3
+# splits over 8.  Lengths: empty, ragged tails, a split shorter than a part.
+@pytest.mark.parametrize("n", [16, 3, 1])
+def test_oneshot_parts_few_items(n):
+    w = W.Workload(name="parts", seed=21, num_seqs=4, num_q_heads=24, num_kv_heads=4,
+                   head_dim=128, block_size=16, seq_lens=(0, 5003, 17, 2048))
+    inp = W.make_paged(w, canary=True)
+    dev = PagedOnDevice(inp)
+    say(f"[parts one-shot] splits={n} lens={list(inp.seq_lens)}")
+    rc, out, ws = dev.run(n)
+    assert rc == P.PDA_OK
+    ref, _, _ = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                               inp.seq_lens, inp.scale)
+    assert_out_close(host_bf16(out), ref, "parts out")
+    if n > 1:
+        _partials_close(inp, ws, n)
+    full = host_bits(out)
+    assert np.all(full[0] == 0)
+    # a second launch finds the tickets at zero: same bytes
+    _, again, _ = dev.run(n)
+    assert np.array_equal(host_bits(again), full)
+    for s in range(4):
+        _, one, _ = dev.run(n, rows=[s])
+        assert np.array_equal(host_bits(one)[0], full[s]), f"seq {s} differs alone (n={n})"
+
+
+def test_oneshot_parts_in_several_launches():
+    """45 sequences at the long-sequence shape need more part records than
+    one launch may use, so the library launches runs of them; each row still
+    matches the oracle and its bytes alone."""
+    w = W.Workload(name="parts-runs", seed=22, num_seqs=45, num_q_heads=24, num_kv_heads=4,
+                   head_dim=128, block_size=16, len_range=(0, 700))
+    inp = W.make_paged(w, canary=True)
+    dev = PagedOnDevice(inp)
+    n = 16
+    say(f"[parts runs] seqs=45 splits={n}")
+    rc, out, _ = dev.run(n)
+    assert rc == P.PDA_OK
+    rows = [0, 1, 19, 20, 21, 22, 41, 42, 43, 44]
+    sub = W.subset_paged(inp, rows)
+    ref, _, _ = A.paged_decode(sub.q, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens,
+                               sub.scale)
+    assert_out_close(host_bf16(out)[rows], ref, "parts runs out")
+    full = host_bits(out)
+    for s in rows:
+        _, one, _ = dev.run(n, rows=[s])
+        assert np.array_equal(host_bits(one)[0], full[s]), f"seq {s} differs alone"
+
+
+# tiled launches never take parts: tiles of any capacity fold in one
+# workgroup per (sequence, head group); checked at several capacities
+@pytest.mark.parametrize("cap", [16, 32, 40, 128])
+def test_tiled_capacities(cap):
+    w = W.Workload(name="tiled-parts", seed=23, num_seqs=8, num_q_heads=16, num_kv_heads=4,
+                   head_dim=256, block_size=32,
+                   seq_lens=(0, 1, 31, 32, 33, 700, 2100, 5000), layout="scratch",
+                   tile_capacity=cap)
+    sc = W.make_scratch(w, canary=True)
+    dev = ScratchOnDevice(sc)
+    say(f"[tiled capacity] capacity={cap}")
+    rows = list(range(8))
+    out, m, l, o = dev.run(cap)
+    ref, rm, rl, ro = A.tiled_state(sc.q, sc.pool, sc.slot_tables, sc.seq_lens)
+    assert_out_close(host_bf16(out), ref, "tiled out")
+    assert_ml_close(m, rm, "state m")
+    assert_ml_close(l, rl, "state l")
+    live = rl > 0
+    assert_out_close(o[live] / l[live][:, None], ro[live] / rl[live][:, None], "state o / l")
+    full = host_bits(out)
+    assert np.all(full[0] == 0)
+    again, *_ = dev.run(cap)
+    assert np.array_equal(host_bits(again), full)
+    for s in rows:
+        one, _, _, _ = dev.run(cap, rows=[s])
+        assert np.array_equal(host_bits(one)[0], full[s]), f"seq {s} differs alone (cap={cap})"
