@@ -98,14 +98,25 @@ size_t lds_per_block() {
 }
 
 // Whether a one-shot launch gives each sequence few workgroups (fewer than
-// 128 (KV head, split) items): such launches get the widest workgroups the
-// kernel allows (12 waves up to 6 heads per group, else 8), within the
-// device's LDS per workgroup.
+// 128 (KV head, split) items): such launches split every item over several
+// workgroups (oneshot_parts) of PDA_FEW_WAVES waves for a BF16 cache (8:
+// measured on the 131072-token sequence with 4 parts, fold 53.5 us against
+// 58.4 us at 12 waves and 59.0 at 6) and PDA_FEW_WAVES_FP8 for an FP8 one,
+// within the kernel's limit and the device's LDS per workgroup.
 bool few_items(uint32_t nkv, uint32_t nsplit) { return (uint64_t)nkv * nsplit < 128; }
 
+// 0: the widest the kernel allows (the FP8 form, half the bytes per token,
+// measured fastest at 12 waves: long-sequence fold 44.8 us vs 47.6 at 8)
+#ifndef PDA_FEW_WAVES
+#define PDA_FEW_WAVES 8
+#endif
+#ifndef PDA_FEW_WAVES_FP8
+#define PDA_FEW_WAVES_FP8 0
+#endif
 int oneshot_waves(uint32_t nkv, uint32_t nsplit, uint32_t head_dim, int gc, bool fp8) {
+    const int few = fp8 ? PDA_FEW_WAVES_FP8 : PDA_FEW_WAVES;
     int w = few_items(nkv, nsplit)
-                ? pda::fold_max_waves(gc)
+                ? (few > 0 && few < pda::fold_max_waves(gc) ? few : pda::fold_max_waves(gc))
                 : (fp8 ? PDA_ONESHOT_WAVES_WIDE_FP8 : PDA_ONESHOT_WAVES_WIDE);
     const size_t cap = lds_per_block();
     while (w > 1 && pda::fold_lds_bytes((int)head_dim, gc, w) > cap) --w;
@@ -253,6 +264,7 @@ pda::PackedParams packed_params(const DecodeShape& s, const void* q, const void*
     p.table_stride = (int)s.max_blocks;
     p.nsplit = (int)nsplit;
     p.c = scale * kLog2e;
+    p.parts = 1;
     return p;
 }
 
@@ -324,6 +336,15 @@ int partials_impl(const DecodeShape& s, const void* q, const void* k, const void
     return rc == PDA_OK ? ok() : rc;
 }
 
+// Workgroups per (sequence, KV head) of the packed kernel's non-split
+// launch (its parts form; 1 = one workgroup each, the pages' launch shape).
+// Measured on 64 sequences of 1K-8K tokens (32 q / 4 kv heads, D 256):
+// 1 part 253 us, 2 parts of 8 waves 213 us (all 512 workgroups resident at
+// once, two per CU), 4 of 4 waves 221 us, 8 parts 280 us and more.
+#ifndef PDA_PACKED_PARTS
+#define PDA_PACKED_PARTS 2
+#endif
+
 // pda_paged_decode and its FP8 form.
 int decode_impl(const DecodeShape& s, const void* q, const void* k, const void* v,
                 const int32_t* bt, const int32_t* lens, void* out, float* ws,
@@ -351,11 +372,25 @@ int decode_impl(const DecodeShape& s, const void* q, const void* k, const void* 
     if (s.num_seqs == 0) return ok();
     const float sc = kv.fp8 ? scale * kv.k_scale : scale;
     if (packed && nsplit == 1) {
+        // PDA_PACKED_PARTS workgroups per (sequence, KV head), a constant,
+        // so a sequence's bytes do not depend on its batch; batches beyond
+        // the library's part records run as several launches
         pda::PackedParams p = packed_params(s, q, k, v, bt, lens, sc, 1);
         p.out = static_cast<uint16_t*>(out);
         p.v_scale = kv.v_scale;
-        hipError_t e = pda::launch_packed(p, s.num_seqs, st, kv.fp8);
-        if (e != hipSuccess) return hip_fail(e, "packed decode launch");
+        p.parts = PDA_PACKED_PARTS;
+        const uint32_t chunk = p.parts > 1 ? pda::packed_part_rows(s.nkv, p.parts) : s.num_seqs;
+        if (chunk == 0) return fail(PDA_EINVAL, "num_kv_heads too large for the packed kernel");
+        for (uint32_t r0 = 0; r0 < s.num_seqs; r0 += chunk) {
+            const uint32_t rows = s.num_seqs - r0 < chunk ? s.num_seqs - r0 : chunk;
+            pda::PackedParams c = p;
+            c.q = p.q + (uint64_t)r0 * s.nq * s.D;
+            c.tables = p.tables + (uint64_t)r0 * s.max_blocks;
+            c.lens = p.lens + r0;
+            c.out = p.out + (uint64_t)r0 * s.nq * s.D;
+            hipError_t e = pda::launch_packed(c, rows, st, kv.fp8);
+            if (e != hipSuccess) return hip_fail(e, "packed decode launch");
+        }
         return ok();
     }
     if (nsplit == 1) {

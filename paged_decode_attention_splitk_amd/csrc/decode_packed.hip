@@ -35,6 +35,13 @@
 // kernels only on non-split launches; the split-K form is this library's
 // extension for long, uneven batches, where one workgroup per sequence and
 // KV head leaves the device waiting on the longest sequence.
+//
+// The parts form (PARTS = true, non-split launches) answers the same
+// imbalance without a workspace or a second launch: p.parts workgroups share
+// one (sequence, KV head), each folding a contiguous run of its blocks into
+// an FP32 record (o unnormalised, m in log2 units, l) of a device array the
+// library owns; the last to take a ticket combines the records in part
+// order and writes the BF16 output.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,6 +57,9 @@ constexpr int kG = 8;              // packed query heads per KV head
 constexpr int kTile = 16;          // tokens per tile
 constexpr int kWaves = 8;          // waves per workgroup, non-split form
 constexpr int kVTileElems = kTile * kD;   // one wave's V tile in LDS (8 KiB)
+#ifndef PDA_PACKED_PARTS_WAVES
+#define PDA_PACKED_PARTS_WAVES 8   /* waves per workgroup of the parts form */
+#endif
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -156,16 +166,38 @@ __device__ __forceinline__ void packed_seq_of_rank(const int32_t* __restrict__ l
 
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <bool SPLIT, int W, bool KV8>
+// Part records (kPackedRec floats each: o [8][256], m [8], l [8], padded to
+// whole 128-byte lines) and arrival tickets of the parts form.  Tickets
+// start at 0 and the combining workgroup puts its ticket back to 0.
+constexpr int kPackedRec = (int)part_rec_floats(kG, kD);
+__device__ __align__(256) float g_packed_sub[kPartSubFloats];
+__device__ __align__(256) uint32_t g_packed_tick[kPartTickets];
+
+// Records are written and read at device scope (write-through stores, loads
+// that do not hit a stale copy), so the hand-over needs no L2 writeback or
+// invalidate: a writer waits for its stores to complete before its
+// workgroup takes a ticket, and the combiner loads after the last ticket.
+__device__ __forceinline__ void put_dev(float* a, float v) {
+    __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_dev(const float* a) {
+    return __hip_atomic_load(const_cast<float*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool SPLIT, int W, bool KV8, bool PARTS>
 __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p) {
+    static_assert(!(SPLIT && PARTS), "parts serve non-split launches");
     constexpr int EB = KV8 ? 1 : 2;   // bytes per cache element
     extern __shared__ __align__(16) uint16_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;   // 16-lane group, lane in group
-    const int kvh = SPLIT ? (int)blockIdx.x % p.nkv : (int)blockIdx.x;
-    const int sp = SPLIT ? (int)blockIdx.x / p.nkv : 0;
+    const int P = PARTS ? p.parts : 1;        // workgroups per (sequence, KV head)
+    const int bx = (int)blockIdx.x / P;
+    const int part = (int)blockIdx.x - bx * P;
+    const int kvh = SPLIT ? bx % p.nkv : bx;
+    const int sp = SPLIT ? bx / p.nkv : 0;
     const int cap = p.table_stride * p.bs;
     int seq, L;
     packed_seq_of_rank(p.lens, (int)gridDim.y, (int)blockIdx.y, cap, seq, L);
@@ -187,6 +219,16 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
             }
             return;
         }
+    }
+    if constexpr (PARTS) {
+        // part i: blocks [i * per, (i + 1) * per) of the sequence, per =
+        // ceil(blocks / parts); possibly none
+        const int nb = (t_end - t_begin + p.bs - 1) / p.bs;
+        const int per = (nb + P - 1) / P;
+        const int64_t fb = (int64_t)t_begin + (int64_t)part * per * p.bs;
+        const int f_begin = fb < t_end ? (int)fb : t_end;
+        t_end = (int64_t)f_begin + (int64_t)per * p.bs < t_end ? f_begin + per * p.bs : t_end;
+        t_begin = f_begin;
     }
 
     // q as the B operand: lane = head c (zeros for the 8 padding heads),
@@ -388,12 +430,81 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
                     slot[kD] = M * kLn2;
                     slot[kD + 1] = Lsum;
                 }
+            } else if constexpr (PARTS) {
+                float* rec = g_packed_sub +
+                             ((int64_t)blockIdx.y * p.nkv * P + blockIdx.x) * kPackedRec;
+                put_dev(rec + h * kD + half * 128 + d2, o0);
+                put_dev(rec + h * kD + half * 128 + d2 + 1, o1);
+                if (half == 0 && d2 == 0) {
+                    put_dev(rec + kG * kD + h, M);
+                    put_dev(rec + kG * kD + kG + h, Lsum);
+                }
             } else {
                 const uint32_t v = Lsum > 0.f ? pack_bf16x2(o0 / Lsum, o1 / Lsum) : 0u;
                 *reinterpret_cast<uint32_t*>(p.out + (q_row + h) * kD + half * 128 + d2) = v;
             }
         }
         __syncthreads();
+    }
+
+    if constexpr (PARTS) {
+        // take a ticket; the last part combines the records in part order
+        // (max over parts with l > 0, weights exp2(m_i - M), weighted sums of
+        // l and o), so the bytes do not depend on arrival order
+        const int64_t item = (int64_t)blockIdx.y * p.nkv + kvh;
+        uint32_t* const tick = g_packed_tick + item;
+        uint32_t* const eT = reinterpret_cast<uint32_t*>(smem);
+        __builtin_amdgcn_s_waitcnt(0);   // this thread's record stores are complete
+        __syncthreads();
+        if (tid == 0)
+            *eT = __hip_atomic_fetch_add(tick, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (*eT != (uint32_t)(P - 1)) return;
+        if (tid == 0) __hip_atomic_store(tick, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float* const recs = g_packed_sub + item * P * kPackedRec;
+        float* const cw = reinterpret_cast<float*>(smem) + 4;   // weights [part][head]
+        float* const cL = cw + kMaxParts * kG;                   // L [head]
+        if (tid < kG) {
+            const int h = tid;
+            float mv[kMaxParts], lv[kMaxParts];
+#pragma unroll
+            for (int i = 0; i < kMaxParts; ++i) {
+                const int ii = i < P ? i : P - 1;
+                mv[i] = get_dev(recs + ii * kPackedRec + kG * kD + h);
+                lv[i] = get_dev(recs + ii * kPackedRec + kG * kD + kG + h);
+            }
+            float M = kNegInf;
+#pragma unroll
+            for (int i = 0; i < kMaxParts; ++i)
+                if (i < P && lv[i] > 0.f) M = fmaxf(M, mv[i]);
+            const float Ms = M == kNegInf ? 0.f : M;
+            float Lsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < kMaxParts; ++i) {
+                if (i < P) {
+                    const float wt = lv[i] > 0.f ? fexp2(mv[i] - Ms) : 0.f;
+                    cw[i * kG + h] = wt;
+                    Lsum += wt * lv[i];
+                }
+            }
+            cL[h] = Lsum;
+        }
+        __syncthreads();
+        for (int i = tid; i < kG * (kD / 2); i += 64 * W) {
+            const int h = i / (kD / 2), d = (i % (kD / 2)) * 2;
+            float o0 = 0.f, o1 = 0.f;
+            for (int c2 = 0; c2 < P; ++c2) {
+                const float wt = cw[c2 * kG + h];
+                if (wt != 0.f) {   // a part that folded nothing is never read
+                    const float* x = recs + c2 * kPackedRec + h * kD + d;
+                    o0 += wt * get_dev(x);
+                    o1 += wt * get_dev(x + 1);
+                }
+            }
+            const float Lsum = cL[h];
+            const uint32_t v = Lsum > 0.f ? pack_bf16x2(o0 / Lsum, o1 / Lsum) : 0u;
+            *reinterpret_cast<uint32_t*>(p.out + (q_row + h) * kD + d) = v;
+        }
     }
 }
 
@@ -409,20 +520,36 @@ hipError_t launch_packed_t(const PackedParams& p, uint32_t num_seqs, hipStream_t
         const int w = p.nsplit >= 12 ? 2 : (p.nsplit >= 3 ? 4 : 8);
         const size_t lds = sizeof(uint16_t) * (size_t)w * kVTileElems;
         if (w == 2)
-            hipLaunchKernelGGL((packed_kernel<true, 2, KV8>), grid, dim3(128), lds, stream, p);
+            hipLaunchKernelGGL((packed_kernel<true, 2, KV8, false>), grid, dim3(128), lds, stream, p);
         else if (w == 4)
-            hipLaunchKernelGGL((packed_kernel<true, 4, KV8>), grid, dim3(256), lds, stream, p);
+            hipLaunchKernelGGL((packed_kernel<true, 4, KV8, false>), grid, dim3(256), lds, stream, p);
         else
-            hipLaunchKernelGGL((packed_kernel<true, 8, KV8>), grid, dim3(512), lds, stream, p);
+            hipLaunchKernelGGL((packed_kernel<true, 8, KV8, false>), grid, dim3(512), lds, stream, p);
+    } else if (p.parts > 1) {
+        // PDA_PACKED_PARTS_WAVES waves per part workgroup
+        if (p.parts > kMaxParts || (uint64_t)num_seqs * p.nkv > kPartTickets ||
+            (uint64_t)num_seqs * p.nkv * p.parts * kPackedRec > kPartSubFloats)
+            return hipErrorInvalidValue;
+        constexpr int w = PDA_PACKED_PARTS_WAVES;
+        const size_t lds = sizeof(uint16_t) * (size_t)w * kVTileElems;
+        hipLaunchKernelGGL((packed_kernel<false, w, KV8, true>),
+                           dim3((uint32_t)(p.nkv * p.parts), num_seqs), dim3(64 * w), lds, stream, p);
     } else {
         const size_t lds = sizeof(uint16_t) * (size_t)kWaves * kVTileElems;   // 64 KiB
-        hipLaunchKernelGGL((packed_kernel<false, kWaves, KV8>), dim3((uint32_t)p.nkv, num_seqs),
+        hipLaunchKernelGGL((packed_kernel<false, kWaves, KV8, false>), dim3((uint32_t)p.nkv, num_seqs),
                            dim3(64 * kWaves), lds, stream, p);
     }
     return hipGetLastError();
 }
 
 }  // namespace
+
+uint32_t packed_part_rows(uint32_t nkv, int parts) {
+    const uint64_t by_tick = kPartTickets / nkv;
+    const uint64_t by_sub = kPartSubFloats / ((uint64_t)nkv * parts * kPackedRec);
+    const uint64_t r = by_tick < by_sub ? by_tick : by_sub;
+    return r > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)r;
+}
 
 hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream,
                          bool kv8) {

@@ -96,7 +96,12 @@ struct PackedParams {
     int nsplit;
     float c;                 // scale * log2(e) (times k_scale for an FP8 cache)
     float v_scale;           // FP8 cache: V = decode(v) * v_scale
+    int parts;               // nsplit == 1: workgroups per (sequence, KV head);
+                             // 1, or up to kMaxParts with the library's records
 };
+// Sequences one packed launch with `parts` parts may carry (the library's
+// part records and tickets).
+uint32_t packed_part_rows(uint32_t nkv, int parts);
 // kv8: k and v hold OCP E4M3 bytes (strides in bytes).
 hipError_t launch_packed(const PackedParams& p, uint32_t num_seqs, hipStream_t stream,
                          bool kv8 = false);

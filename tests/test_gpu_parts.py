@@ -4,8 +4,9 @@ workgroups, whose last one to finish combines their records.  Checked
 against the FP64 oracle, for batch invariance (a sequence's bytes alone and
 co-batched, also across runs of sequences that the library launches
 separately), and for repeatability (the arrival tickets are back at zero
-after every launch).  Tiled launches, which never take parts, are checked
-at several tile capacities.  Needs an MI355X."""
+after every launch).  The GQA-packed MFMA kernel's non-split launch has the
+same form.  Tiled launches, which never take parts, are checked at several
+tile capacities.  Needs an MI355X."""
 import numpy as np
 import pytest
 
@@ -115,3 +116,29 @@ def test_tiled_capacities(cap):
     for s in rows:
         one, _, _, _ = dev.run(cap, rows=[s])
         assert np.array_equal(host_bits(one)[0], full[s]), f"seq {s} differs alone (cap={cap})"
+
+
+def test_packed_parts_in_several_launches():
+    """The packed MFMA kernel's non-split launch splits each (sequence, KV
+    head) over 2 workgroups; 300 sequences of the packed shape need more part
+    records than one launch may use, so the library runs several launches.
+    Sampled rows match the oracle, every sampled row has the same bytes
+    alone, and a repeated call gives the same bytes (tickets back at 0)."""
+    w = W.Workload(name="packed-runs", seed=24, num_seqs=300, num_q_heads=32, num_kv_heads=4,
+                   head_dim=256, block_size=16, len_range=(0, 400))
+    inp = W.make_paged(w, canary=True)
+    dev = PagedOnDevice(inp)
+    say("[packed parts runs] seqs=300")
+    rc, out, _ = dev.run(1, packed=True)
+    assert rc == P.PDA_OK
+    rows = [0, 1, 150, 250, 251, 252, 253, 299]
+    sub = W.subset_paged(inp, rows)
+    ref, _, _ = A.paged_decode(sub.q, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens,
+                               sub.scale)
+    assert_out_close(host_bf16(out)[rows], ref, "packed parts runs")
+    full = host_bits(out)
+    _, again, _ = dev.run(1, packed=True)
+    assert np.array_equal(host_bits(again), full)
+    for s in rows:
+        _, one, _ = dev.run(1, packed=True, rows=[s])
+        assert np.array_equal(host_bits(one)[0], full[s]), f"packed seq {s} differs alone"
