@@ -271,9 +271,9 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
                 MODE == kModeTiled ? p.table_stride : p.table_stride * p.bs, seq, slen);
     const int per_seq = p.nkv * p.HG;
     static_assert(!(PARTS && MODE == kModeTiled), "tiled launches take no parts");
-    const int P = PARTS ? p.parts : 1;            // workgroups per item
-    const int bx = (int)blockIdx.x / P;           // the item's index in the row
-    const int part = (int)blockIdx.x - bx * P;
+    const int PL = PARTS ? p.parts : 1;           // workgroups per item in the grid
+    const int bx = (int)blockIdx.x / PL;          // the item's index in the row
+    const int part = (int)blockIdx.x - bx * PL;
     const int kvhg = MODE == kModeTiled ? bx : bx % per_seq;
     const int split = MODE == kModeTiled ? 0 : bx / per_seq;
     const int kvh = kvhg / p.HG, hg = kvhg % p.HG;
@@ -358,6 +358,17 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
     // This workgroup's run of the item: with parts, part i folds blocks
     // [i * per, (i + 1) * per) of the item (per = ceil(blocks / parts)),
     // possibly none.
+    // The parts an item uses: at most PL, and no more than one per
+    // kMinPartBlocks of its blocks (short items gain nothing from the
+    // hand-over); a function of the sequence's own length, so its bytes do
+    // not depend on the batch.  Parts past that count have nothing to do.
+    int P = PL;
+    if (PARTS) {
+        const int nb_item = (t_end - t_begin + p.bs - 1) / p.bs;
+        const int want = (nb_item + kMinPartBlocks - 1) / kMinPartBlocks;
+        P = want < PL ? (want > 1 ? want : 1) : PL;
+        if (part >= P) return;
+    }
     if (P > 1) {
         const int nb_item = (t_end - t_begin + p.bs - 1) / p.bs;
         const int per = (nb_item + P - 1) / P;
@@ -643,10 +654,10 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
     constexpr bool with_old = MODE == kModeTiled;
     const int64_t row_q = (int64_t)seq * p.nq + h0;  // first q slot of the group
     // this part's record: o [GC][D], m [GC] (log2 units), l [GC]
-    const int64_t item = (int64_t)blockIdx.y * (gridDim.x / P) + bx;
+    const int64_t item = (int64_t)blockIdx.y * (gridDim.x / PL) + bx;
     constexpr int REC = (int)part_rec_floats(GC, D);
     float* const psub = p.sub ? p.sub : g_part_sub;
-    float* const prec = psub + (item * P + part) * REC;
+    float* const prec = psub + (item * PL + part) * REC;
     if (tid < gcount) {
         const int h = tid;
         float M = kNegInf, m_old = kNegInf, m2_old = kNegInf, l_old = 0.f;
@@ -754,7 +765,7 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
         __syncthreads();
         if (*eT != (uint32_t)(P - 1)) return;
         if (tid == 0) __hip_atomic_store(tick, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float* const recs = psub + item * P * REC;
+        const float* const recs = psub + item * PL * REC;
         // weights: ew[i * GC + h] for part i
         if (tid < gcount) {
             const int h = tid;

@@ -193,9 +193,9 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c = lane & 15;   // 16-lane group, lane in group
-    const int P = PARTS ? p.parts : 1;        // workgroups per (sequence, KV head)
-    const int bx = (int)blockIdx.x / P;
-    const int part = (int)blockIdx.x - bx * P;
+    const int PL = PARTS ? p.parts : 1;       // workgroups per (sequence, KV head) in the grid
+    const int bx = (int)blockIdx.x / PL;
+    const int part = (int)blockIdx.x - bx * PL;
     const int kvh = SPLIT ? bx % p.nkv : bx;
     const int sp = SPLIT ? bx / p.nkv : 0;
     const int cap = p.table_stride * p.bs;
@@ -220,7 +220,17 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
             return;
         }
     }
+    // The parts this sequence uses: at most PL, no more than one per
+    // kMinPartBlocks of its blocks (a function of its own length, so its
+    // bytes do not depend on the batch); parts past that count exit.
+    int P = 1;
     if constexpr (PARTS) {
+        const int nb = (t_end - t_begin + p.bs - 1) / p.bs;
+        const int want = (nb + kMinPartBlocks - 1) / kMinPartBlocks;
+        P = want < PL ? (want > 1 ? want : 1) : PL;
+        if (part >= P) return;
+    }
+    if (P > 1) {
         // part i: blocks [i * per, (i + 1) * per) of the sequence, per =
         // ceil(blocks / parts); possibly none
         const int nb = (t_end - t_begin + p.bs - 1) / p.bs;
@@ -430,9 +440,9 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
                     slot[kD] = M * kLn2;
                     slot[kD + 1] = Lsum;
                 }
-            } else if constexpr (PARTS) {
+            } else if (PARTS && P > 1) {
                 float* rec = g_packed_sub +
-                             ((int64_t)blockIdx.y * p.nkv * P + blockIdx.x) * kPackedRec;
+                             ((int64_t)blockIdx.y * p.nkv * PL + blockIdx.x) * kPackedRec;
                 put_dev(rec + h * kD + half * 128 + d2, o0);
                 put_dev(rec + h * kD + half * 128 + d2 + 1, o1);
                 if (half == 0 && d2 == 0) {
@@ -447,7 +457,7 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
         __syncthreads();
     }
 
-    if constexpr (PARTS) {
+    if (PARTS && P > 1) {
         // take a ticket; the last part combines the records in part order
         // (max over parts with l > 0, weights exp2(m_i - M), weighted sums of
         // l and o), so the bytes do not depend on arrival order
@@ -461,7 +471,7 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
         __syncthreads();
         if (*eT != (uint32_t)(P - 1)) return;
         if (tid == 0) __hip_atomic_store(tick, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float* const recs = g_packed_sub + item * P * kPackedRec;
+        const float* const recs = g_packed_sub + item * PL * kPackedRec;
         float* const cw = reinterpret_cast<float*>(smem) + 4;   // weights [part][head]
         float* const cL = cw + kMaxParts * kG;                   // L [head]
         if (tid < kG) {

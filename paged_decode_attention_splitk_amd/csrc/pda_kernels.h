@@ -49,7 +49,9 @@ struct FoldParams {
 constexpr int kMaxHeadsPerGroup = 8;
 
 // Most parts per item, and the capacity of the library's own part arrays.
+// An item uses no more parts than it has runs of kMinPartBlocks blocks.
 constexpr int kMaxParts = 8;
+constexpr int kMinPartBlocks = 32;
 constexpr uint64_t kPartTickets = 1u << 16;
 constexpr uint64_t kPartSubFloats = 1u << 22;   // 16 MiB
 // Floats of one part record for gc heads of head_dim d: o [gc][d], m [gc],

@@ -41,8 +41,10 @@ def _partials_close(inp, ws, n):
 
 
 # 24 q / 4 kv heads at D 128 (the long-sequence shape): at 16 splits a
-# sequence has 64 items, so each is split over 4 workgroups; at 1 and 3
-# splits over 8.  Lengths: empty, ragged tails, a split shorter than a part.
+# sequence has 64 items, so the grid gives each 4 workgroups; at 1 and 3
+# splits 8.  An item uses one part per 32 of its blocks, up to that: here
+# 1 (16 splits), 2 or 4 (3 splits), 4 or 8 (1 split).  Lengths: empty,
+# ragged tails, a split shorter than a part.
 @pytest.mark.parametrize("n", [16, 3, 1])
 def test_oneshot_parts_few_items(n):
     w = W.Workload(name="parts", seed=21, num_seqs=4, num_q_heads=24, num_kv_heads=4,
@@ -120,12 +122,16 @@ def test_tiled_capacities(cap):
 
 def test_packed_parts_in_several_launches():
     """The packed MFMA kernel's non-split launch splits each (sequence, KV
-    head) over 2 workgroups; 300 sequences of the packed shape need more part
-    records than one launch may use, so the library runs several launches.
+    head) of 33 blocks or more over 2 workgroups; 300 sequences of the packed
+    shape need more part records than one launch may use, so the library runs
+    several launches.
     Sampled rows match the oracle, every sampled row has the same bytes
     alone, and a repeated call gives the same bytes (tickets back at 0)."""
+    # most sequences are short (one part: under 64 blocks); the forced long
+    # ones use 2 parts, on both sides of the launch boundary at 252 rows
     w = W.Workload(name="packed-runs", seed=24, num_seqs=300, num_q_heads=32, num_kv_heads=4,
-                   head_dim=256, block_size=16, len_range=(0, 400))
+                   head_dim=256, block_size=16, len_range=(0, 400),
+                   forced=((0, 1500), (251, 1200), (252, 2000), (299, 900)))
     inp = W.make_paged(w, canary=True)
     dev = PagedOnDevice(inp)
     say("[packed parts runs] seqs=300")
