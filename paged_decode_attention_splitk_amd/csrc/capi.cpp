@@ -165,6 +165,7 @@ hipError_t launch_oneshot(int mode, const DecodeShape& s, int gc, int hg, pda::F
     const int parts = oneshot_parts(s.nkv, (uint32_t)hg, nsplit, gc, s.D);
     const uint64_t items = (uint64_t)s.nkv * hg * nsplit;
     p.parts = parts;
+    p.part_min = pda::kMinPartBlocks;
     p.sub = nullptr;
     p.tick = nullptr;
     const uint32_t gx = (uint32_t)(items * parts);
@@ -186,6 +187,23 @@ hipError_t launch_oneshot(int mode, const DecodeShape& s, int gc, int hg, pda::F
 #ifndef PDA_TILED_WAVES
 #define PDA_TILED_WAVES 8
 #endif
+// Parts per tile of a tiled launch: up to PDA_TILED_PARTS, one per
+// kMinTilePartBlocks blocks of the sequence's own tile, so a full tile of the
+// later calls of a step (which hold only the longer sequences) still spreads
+// over the chip while a call that folds one partial last block per
+// sequence runs one workgroup each, with no hand-over.  Measured on 128
+// sequences of 0-16K tokens, 64-block tiles: 1 part 1134 us per step, 2
+// parts 1103, 3 parts 1079, 4 parts 1100 (each part workgroup in the grid
+// costs the partial-block calls dispatch time).
+#ifndef PDA_TILED_PARTS
+#define PDA_TILED_PARTS 3
+#endif
+int tiled_parts(const pda_tiled_dims& d) {
+    uint32_t parts = (d.tile_capacity + pda::kMinTilePartBlocks - 1) / pda::kMinTilePartBlocks;
+    if (parts > PDA_TILED_PARTS) parts = PDA_TILED_PARTS;
+    return parts < 2 ? 1 : (int)parts;
+}
+
 int tiled_waves(uint32_t head_dim, int gc) {
     int w = PDA_TILED_WAVES;
     while (w > 1 && pda::fold_lds_bytes((int)head_dim, gc, w) > 64 * 1024) --w;
@@ -566,6 +584,9 @@ struct pda_tiled {
     float* m;
     float* l;
     float* o;
+    int parts;        // workgroups per (sequence, head group) tile
+    float* sub;       // part records (parts > 1)
+    uint32_t* tick;   // arrival tickets, zeroed at creation (parts > 1)
 };
 
 extern "C" {
@@ -607,6 +628,17 @@ int pda_tiled_create(const pda_tiled_dims* d, pda_tiled** out) {
     e = hipMalloc((void**)&t->m, slots * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void**)&t->l, slots * sizeof(float));
     if (e == hipSuccess) e = hipMalloc((void**)&t->o, slots * d->head_dim * sizeof(float));
+    t->parts = tiled_parts(*d);
+    if (t->parts > 1 && e == hipSuccess) {
+        int hg = 0;
+        const int gc = head_groups(d->num_q_heads / d->num_kv_heads, &hg);
+        const uint64_t items = (uint64_t)d->max_seqs * d->num_kv_heads * hg;
+        e = hipMalloc((void**)&t->sub, items * t->parts *
+                                           pda::part_rec_floats(gc, (int)d->head_dim) *
+                                           sizeof(float));
+        if (e == hipSuccess) e = hipMalloc((void**)&t->tick, items * sizeof(uint32_t));
+        if (e == hipSuccess) e = hipMemset(t->tick, 0, items * sizeof(uint32_t));
+    }
     if (e != hipSuccess) {
         pda_tiled_destroy(t);
         return e == hipErrorOutOfMemory ? fail(PDA_ENOMEM, "tiled state allocation failed")
@@ -621,6 +653,8 @@ void pda_tiled_destroy(pda_tiled* t) {
     if (t->m) (void)hipFree(t->m);
     if (t->l) (void)hipFree(t->l);
     if (t->o) (void)hipFree(t->o);
+    if (t->sub) (void)hipFree(t->sub);
+    if (t->tick) (void)hipFree(t->tick);
     delete t;
 }
 
@@ -704,10 +738,13 @@ int pda_tiled_step_tile(pda_tiled* t, const void* q, const void* k_pool, const v
     p.lbvs = last_block_valid_slots;
     // the step takes no scale: 1 / sqrt(head_dim), rounded once to FP32
     p.c = (float)(1.0 / std::sqrt((double)d.head_dim)) * kLog2e;
-    p.parts = 1;
+    p.parts = t->parts;
+    p.part_min = pda::kMinTilePartBlocks;
+    p.sub = t->sub;
+    p.tick = t->tick;
     const int waves = tiled_waves(d.head_dim, gc);
     hipError_t e = pda::launch_fold(pda::kModeTiled, (int)d.head_dim, gc, p,
-                                    (uint32_t)(d.num_kv_heads * hg), num_seqs, waves,
+                                    (uint32_t)(d.num_kv_heads * hg * t->parts), num_seqs, waves,
                                     (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "step_tile launch");
     return ok();

@@ -270,7 +270,6 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
     seq_of_rank(p.lens, (int)gridDim.y, (int)blockIdx.y,
                 MODE == kModeTiled ? p.table_stride : p.table_stride * p.bs, seq, slen);
     const int per_seq = p.nkv * p.HG;
-    static_assert(!(PARTS && MODE == kModeTiled), "tiled launches take no parts");
     const int PL = PARTS ? p.parts : 1;           // workgroups per item in the grid
     const int bx = (int)blockIdx.x / PL;          // the item's index in the row
     const int part = (int)blockIdx.x - bx * PL;
@@ -359,13 +358,13 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
     // [i * per, (i + 1) * per) of the item (per = ceil(blocks / parts)),
     // possibly none.
     // The parts an item uses: at most PL, and no more than one per
-    // kMinPartBlocks of its blocks (short items gain nothing from the
+    // p.part_min of its blocks (short items gain nothing from the
     // hand-over); a function of the sequence's own length, so its bytes do
     // not depend on the batch.  Parts past that count have nothing to do.
     int P = PL;
     if (PARTS) {
         const int nb_item = (t_end - t_begin + p.bs - 1) / p.bs;
-        const int want = (nb_item + kMinPartBlocks - 1) / kMinPartBlocks;
+        const int want = (nb_item + p.part_min - 1) / p.part_min;
         P = want < PL ? (want > 1 ? want : 1) : PL;
         if (part >= P) return;
     }
@@ -649,9 +648,10 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
     }
     __syncthreads();
 
-    // Per head: the workgroup max, every contributor's weight, and l (and
-    // the running state of a tiled launch, which never has parts).
-    constexpr bool with_old = MODE == kModeTiled;
+    // Per head: the workgroup max, every contributor's weight, and l, and
+    // the running state of a tiled launch (when the item is split into
+    // parts, the state joins when they are combined).
+    const bool with_old = MODE == kModeTiled && P == 1;
     const int64_t row_q = (int64_t)seq * p.nq + h0;  // first q slot of the group
     // this part's record: o [GC][D], m [GC] (log2 units), l [GC]
     const int64_t item = (int64_t)blockIdx.y * (gridDim.x / PL) + bx;
@@ -752,9 +752,9 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
     if (P == 1) return;
 
     // Parts: publish this record, take a ticket; the last part to arrive
-    // combines every part's record, in part order, with the same weighting,
-    // so the result depends on the item's data and the part count only,
-    // never on arrival order.
+    // combines every part's record, in part order, with the same weighting
+    // (after the running state, for a tiled launch), so the result depends
+    // on the item's data and the part count only, never on arrival order.
     if constexpr (PARTS) {
         uint32_t* const tick = (p.tick ? p.tick : g_part_tick) + item;
         uint32_t* const eT = reinterpret_cast<uint32_t*>(eL + GC);
@@ -766,10 +766,16 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
         if (*eT != (uint32_t)(P - 1)) return;
         if (tid == 0) __hip_atomic_store(tick, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const float* const recs = psub + item * PL * REC;
-        // weights: ew[i * GC + h] for part i
+        // weights: ew[i * GC + h] for part i, ew[P * GC + h] for the state
         if (tid < gcount) {
             const int h = tid;
-            float M = kNegInf;
+            float M = kNegInf, m_old = kNegInf, m2_old = kNegInf, l_old = 0.f;
+            if constexpr (MODE == kModeTiled) {
+                m_old = p.ws[row_q + h];
+                l_old = p.l_state[row_q + h];
+                m2_old = m_old * kLog2e;
+                M = m2_old;
+            }
             float mv[kMaxParts], lv[kMaxParts];
 #pragma unroll
             for (int i = 0; i < kMaxParts; ++i) {
@@ -782,6 +788,11 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
                 if (i < P && lv[i] > 0.f) M = fmaxf(M, mv[i]);
             const float Ms = M == kNegInf ? 0.f : M;
             float L = 0.f;
+            if constexpr (MODE == kModeTiled) {
+                const float wo = fexp2(m2_old - Ms);
+                ew[P * GC + h] = wo;
+                L = wo * l_old;
+            }
 #pragma unroll
             for (int i = 0; i < kMaxParts; ++i) {
                 if (i < P) {
@@ -796,6 +807,10 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
                 float* slot = p.ws + ((row_q + h) * p.nsplit + split) * (int64_t)(D + 2);
                 slot[D] = M * kLn2;
                 slot[D + 1] = L;
+            } else if constexpr (MODE == kModeTiled) {
+                // keep the stored max bit-identical when this tile did not raise it
+                p.ws[row_q + h] = M == m2_old ? m_old : M * kLn2;
+                p.l_state[row_q + h] = L;
             }
         }
         __syncthreads();
@@ -804,6 +819,12 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
             const int d = (i - h * (D / 2)) * 2;
             float o0 = 0.f, o1 = 0.f;
             const int64_t qs = row_q + h;
+            if constexpr (MODE == kModeTiled) {
+                const float2 prev = *reinterpret_cast<const float2*>(p.o_state + qs * D + d);
+                const float wo = ew[P * GC + h];
+                o0 = wo * prev.x;
+                o1 = wo * prev.y;
+            }
             for (int c = 0; c < P; ++c) {
                 const float wt = ew[c * GC + h];
                 if (wt != 0.f) {   // an empty part's o is never read
@@ -818,9 +839,11 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
                     float* slot = p.ws + (qs * p.nsplit + split) * (int64_t)(D + 2);
                     *reinterpret_cast<float2*>(slot + d) = make_float2(o0, o1);
                 }
-            } else {
+            } else if constexpr (MODE == kModeFinal) {
                 const uint32_t v = L > 0.f ? pack_bf16x2(o0 / L, o1 / L) : 0u;
                 *reinterpret_cast<uint32_t*>(p.out + qs * D + d) = v;
+            } else {
+                *reinterpret_cast<float2*>(p.o_state + qs * D + d) = make_float2(o0, o1);
             }
         }
     }
@@ -999,12 +1022,16 @@ hipError_t launch_fold(int mode, int head_dim, int gc, const FoldParams& p, uint
     switch (mode) {
         case kModePartial: fn = pick_oneshot<kModePartial>(head_dim, gc, kv8, parts); break;
         case kModeFinal: fn = pick_oneshot<kModeFinal>(head_dim, gc, kv8, parts); break;
-        case kModeTiled: fn = kv8 ? nullptr : pick_d<kModeTiled, false>(head_dim, gc); break;
+        case kModeTiled:
+            fn = kv8 ? nullptr
+                     : (parts ? pick_d<kModeTiled, false, true>(head_dim, gc)
+                              : pick_d<kModeTiled, false>(head_dim, gc));
+            break;
         default: break;
     }
     if (!fn || waves < 1 || 64 * waves > fold_max_threads(gc)) return hipErrorInvalidValue;
     if (p.parts < 1 || p.parts > kMaxParts || grid_x % (uint32_t)p.parts != 0 ||
-        (mode == kModeTiled && p.parts != 1))
+        (p.parts > 1 && p.part_min < 1))
         return hipErrorInvalidValue;
     const size_t lds = fold_lds_bytes(head_dim, gc, waves);
     if (lds > 64 * 1024) {

@@ -33,14 +33,16 @@ struct FoldParams {
     int lbvs;                // valid slots of a tile's last block (tiled)
     float c;                 // scale * log2(e) (times k_scale for an FP8 cache)
     float v_scale;           // FP8 cache only: V = decode(v8) * v_scale
-    // Parts (one-shot launches only): `parts` workgroups share one item (one
-    // split of one sequence and head group), each folding a contiguous run
-    // of its blocks into a record of `sub`; the last to arrive (ticket in
+    // Parts: `parts` workgroups share one item (one split of one sequence
+    // and head group, or one sequence's tile), of which an item of n blocks
+    // uses min(parts, ceil(n / part_min)), each folding a contiguous run of
+    // its blocks into a record of `sub`; the last to arrive (ticket in
     // `tick`) combines the records in part order and writes what one
     // workgroup would.  parts == 1: no records, no tickets.  Null sub /
     // tick: the library's own device arrays (kPartSubFloats / kPartTickets
     // entries).
     int parts;
+    int part_min;            // blocks per part at least (parts > 1)
     float* sub;              // [item][part] records (part_rec_floats each)
     uint32_t* tick;          // [item] arrival counters, 0 between launches
 };
@@ -49,9 +51,11 @@ struct FoldParams {
 constexpr int kMaxHeadsPerGroup = 8;
 
 // Most parts per item, and the capacity of the library's own part arrays.
-// An item uses no more parts than it has runs of kMinPartBlocks blocks.
+// A one-shot item uses no more parts than it has runs of kMinPartBlocks
+// blocks (the packed kernel likewise); a tile, runs of kMinTilePartBlocks.
 constexpr int kMaxParts = 8;
 constexpr int kMinPartBlocks = 32;
+constexpr int kMinTilePartBlocks = 16;
 constexpr uint64_t kPartTickets = 1u << 16;
 constexpr uint64_t kPartSubFloats = 1u << 22;   // 16 MiB
 // Floats of one part record for gc heads of head_dim d: o [gc][d], m [gc],

@@ -4,9 +4,9 @@ workgroups, whose last one to finish combines their records.  Checked
 against the FP64 oracle, for batch invariance (a sequence's bytes alone and
 co-batched, also across runs of sequences that the library launches
 separately), and for repeatability (the arrival tickets are back at zero
-after every launch).  The GQA-packed MFMA kernel's non-split launch has the
-same form.  Tiled launches, which never take parts, are checked at several
-tile capacities.  Needs an MI355X."""
+after every launch).  The GQA-packed MFMA kernel's non-split launch and the
+tiled step have the same form (the tiled one with the running state joining
+the combine), checked at several tile capacities.  Needs an MI355X."""
 import numpy as np
 import pytest
 
@@ -92,8 +92,9 @@ def test_oneshot_parts_in_several_launches():
         assert np.array_equal(host_bits(one)[0], full[s]), f"seq {s} differs alone"
 
 
-# tiled launches never take parts: tiles of any capacity fold in one
-# workgroup per (sequence, head group); checked at several capacities
+# tiled launches: capacity 16 gives 1 part per tile, 32 gives 2, 40 and 128
+# give 3; a sequence's tile of n blocks uses one part per 16 of them, up to
+# that (so 1-block tail tiles fold in one workgroup)
 @pytest.mark.parametrize("cap", [16, 32, 40, 128])
 def test_tiled_capacities(cap):
     w = W.Workload(name="tiled-parts", seed=23, num_seqs=8, num_q_heads=16, num_kv_heads=4,
