@@ -34,7 +34,11 @@ def _capture(fn):
     return g
 
 
-@pytest.mark.parametrize("n,flags", [(1, "unpacked"), (16, "unpacked"), (4, "packed")])
+# 1 unpacked: 8 parts per item (4 KV heads); 16 unpacked: 4 parts; 1 packed:
+# the packed kernel's 2 parts (sequences of 33 blocks or more); 4 packed:
+# its split-K form
+@pytest.mark.parametrize("n,flags", [(1, "unpacked"), (16, "unpacked"), (1, "packed"),
+                                     (4, "packed")])
 def test_decode_graph_replays(n, flags):
     say(f"[graph] splits={n} {flags}")
     base = W.Workload(name="graph", seed=30, num_seqs=12, num_q_heads=32, num_kv_heads=4,

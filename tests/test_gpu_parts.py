@@ -149,3 +149,32 @@ def test_packed_parts_in_several_launches():
     for s in rows:
         _, one, _ = dev.run(1, packed=True, rows=[s])
         assert np.array_equal(host_bits(one)[0], full[s]), f"packed seq {s} differs alone"
+
+
+def test_part_users_interleaved():
+    """Launches that hand records over (a few-item split-K fold, the packed
+    non-split kernel, a tiled step) run one after another on one stream in
+    several orders; each gives the bytes it gives alone, so none leaves a
+    ticket or record behind that another one reads."""
+    lw = W.Workload(name="mix-long", seed=25, num_seqs=2, num_q_heads=24, num_kv_heads=4,
+                    head_dim=128, block_size=16, seq_lens=(3000, 1200))
+    pw = W.Workload(name="mix-packed", seed=26, num_seqs=3, num_q_heads=32, num_kv_heads=4,
+                    head_dim=256, block_size=16, seq_lens=(900, 40, 1700))
+    tw = W.Workload(name="mix-tiled", seed=27, num_seqs=3, num_q_heads=16, num_kv_heads=4,
+                    head_dim=256, block_size=32, seq_lens=(2500, 0, 700), layout="scratch",
+                    tile_capacity=64)
+    ld = PagedOnDevice(W.make_paged(lw, canary=True))
+    pd = PagedOnDevice(W.make_paged(pw, canary=True))
+    td = ScratchOnDevice(W.make_scratch(tw, canary=True))
+    say("[parts interleaved]")
+    base_l = host_bits(ld.run(3)[1])
+    base_p = host_bits(pd.run(1, packed=True)[1])
+    base_t = host_bits(td.run(64)[0])
+    for order in ("lpt", "tpl", "ptl", "llpptt"):
+        for c in order:
+            if c == "l":
+                assert np.array_equal(host_bits(ld.run(3)[1]), base_l), order
+            elif c == "p":
+                assert np.array_equal(host_bits(pd.run(1, packed=True)[1]), base_p), order
+            else:
+                assert np.array_equal(host_bits(td.run(64)[0]), base_t), order
