@@ -157,15 +157,38 @@ uint32_t part_rows(uint64_t items_per_row, int parts, int gc, uint32_t head_dim)
     return r > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)r;
 }
 
+// Blocks per part at least, for one-shot launches.  Measured: the
+// 131072-token sequence is as fast at 128 as at 32 (58.2 vs 59.8 us), while
+// 64 sequences at 4 splits (head dim 256, 8 heads per KV head), which need
+// no parts, took 447 / 350 / 276 us at 32 / 64 / 128 (271 without parts).
+#ifndef PDA_PART_MIN
+#define PDA_PART_MIN 128
+#endif
+
+// Part workgroups the grid needs per item: an item of n blocks uses
+// min(cap, ceil(n / part_min)) of them, and no item of this launch has more
+// blocks than the largest split a table row of max_blocks blocks allows, so
+// the grid carries no part slot that no item can use (such slots are not
+// free: 64 sequences at head dim 256 and 16 splits, where every item uses
+// one part, took 1196 us with 4 slots per item against 357 us with one).
+// The parts an item uses do not depend on this count, only on its length.
+int grid_parts(int cap, uint32_t max_blocks, uint32_t nsplit, uint32_t bs, int part_min) {
+    if (cap <= 1) return 1;
+    const uint32_t most = pda::split_chunk(max_blocks * bs, nsplit, bs) / bs;  // blocks
+    const uint32_t need = (most + part_min - 1) / part_min;
+    return need < 2 ? 1 : (need < (uint32_t)cap ? (int)need : cap);
+}
+
 // Launches a one-shot fold over all sequences; with parts, in runs of
 // sequences that fit the library's part arrays (each run is an ordinary
 // launch over fewer rows: a sequence's arithmetic does not change).
 hipError_t launch_oneshot(int mode, const DecodeShape& s, int gc, int hg, pda::FoldParams p,
                           uint32_t nsplit, int waves, hipStream_t stream, bool kv8) {
-    const int parts = oneshot_parts(s.nkv, (uint32_t)hg, nsplit, gc, s.D);
+    const int cap = oneshot_parts(s.nkv, (uint32_t)hg, nsplit, gc, s.D);
+    const int parts = grid_parts(cap, s.max_blocks, nsplit, s.bs, PDA_PART_MIN);
     const uint64_t items = (uint64_t)s.nkv * hg * nsplit;
     p.parts = parts;
-    p.part_min = pda::kMinPartBlocks;
+    p.part_min = PDA_PART_MIN;
     p.sub = nullptr;
     p.tick = nullptr;
     const uint32_t gx = (uint32_t)(items * parts);
@@ -396,7 +419,7 @@ int decode_impl(const DecodeShape& s, const void* q, const void* k, const void* 
         pda::PackedParams p = packed_params(s, q, k, v, bt, lens, sc, 1);
         p.out = static_cast<uint16_t*>(out);
         p.v_scale = kv.v_scale;
-        p.parts = PDA_PACKED_PARTS;
+        p.parts = grid_parts(PDA_PACKED_PARTS, s.max_blocks, 1, s.bs, pda::kMinPartBlocks);
         const uint32_t chunk = p.parts > 1 ? pda::packed_part_rows(s.nkv, p.parts) : s.num_seqs;
         if (chunk == 0) return fail(PDA_EINVAL, "num_kv_heads too large for the packed kernel");
         for (uint32_t r0 = 0; r0 < s.num_seqs; r0 += chunk) {

@@ -34,15 +34,20 @@ def _capture(fn):
     return g
 
 
-# 1 unpacked: 8 parts per item (4 KV heads); 16 unpacked: 4 parts; 1 packed:
-# the packed kernel's 2 parts (sequences of 33 blocks or more); 4 packed:
-# its split-K form
+# 1 packed: the packed kernel's 2 parts (sequences of 33 blocks or more);
+# 4 packed: its split-K form; "long": 24 q / 4 kv heads at D 128 with a
+# 40000-token sequence, whose items use 2 parts at 16 splits and 8 at 1
 @pytest.mark.parametrize("n,flags", [(1, "unpacked"), (16, "unpacked"), (1, "packed"),
-                                     (4, "packed")])
+                                     (4, "packed"), (16, "long"), (1, "long")])
 def test_decode_graph_replays(n, flags):
     say(f"[graph] splits={n} {flags}")
-    base = W.Workload(name="graph", seed=30, num_seqs=12, num_q_heads=32, num_kv_heads=4,
-                      head_dim=256, block_size=16, len_range=(1, 1500))
+    if flags == "long":
+        base = W.Workload(name="graph-long", seed=32, num_seqs=3, num_q_heads=24,
+                          num_kv_heads=4, head_dim=128, block_size=16,
+                          seq_lens=(40000, 9000, 300))
+    else:
+        base = W.Workload(name="graph", seed=30, num_seqs=12, num_q_heads=32, num_kv_heads=4,
+                          head_dim=256, block_size=16, len_range=(1, 1500))
     inp = W.make_paged(base, canary=True)
     dev = PagedOnDevice(inp)
     S, nq, D = inp.num_seqs, inp.num_q_heads, inp.head_dim

@@ -41,14 +41,15 @@ def _partials_close(inp, ws, n):
 
 
 # 24 q / 4 kv heads at D 128 (the long-sequence shape): at 16 splits a
-# sequence has 64 items, so the grid gives each 4 workgroups; at 1 and 3
-# splits 8.  An item uses one part per 32 of its blocks, up to that: here
-# 1 (16 splits), 2 or 4 (3 splits), 4 or 8 (1 split).  Lengths: empty,
-# ragged tails, a split shorter than a part.
+# sequence has 64 items, so an item may use 4 workgroups; at 1 and 3 splits
+# 8.  An item uses one part per 128 of its blocks, up to that: the
+# 40000-token sequence 2 (16 splits), 7 (3 splits) or 8 (1 split); the
+# 9000-token one 1, 2 or 5.  Lengths: empty, ragged tails, a split shorter
+# than a part.
 @pytest.mark.parametrize("n", [16, 3, 1])
 def test_oneshot_parts_few_items(n):
     w = W.Workload(name="parts", seed=21, num_seqs=4, num_q_heads=24, num_kv_heads=4,
-                   head_dim=128, block_size=16, seq_lens=(0, 5003, 17, 2048))
+                   head_dim=128, block_size=16, seq_lens=(0, 40000, 17, 9000))
     inp = W.make_paged(w, canary=True)
     dev = PagedOnDevice(inp)
     say(f"[parts one-shot] splits={n} lens={list(inp.seq_lens)}")
@@ -70,18 +71,19 @@ def test_oneshot_parts_few_items(n):
 
 
 def test_oneshot_parts_in_several_launches():
-    """45 sequences at the long-sequence shape need more part records than
-    one launch may use, so the library launches runs of them; each row still
-    matches the oracle and its bytes alone."""
+    """45 sequences at the long-sequence shape, one of 40000 tokens (so an
+    item may use 2 parts at 16 splits), need more part records than one
+    launch may use, so the library launches runs of them (40 rows, then 5);
+    each row still matches the oracle and its bytes alone."""
     w = W.Workload(name="parts-runs", seed=22, num_seqs=45, num_q_heads=24, num_kv_heads=4,
-                   head_dim=128, block_size=16, len_range=(0, 700))
+                   head_dim=128, block_size=16, len_range=(0, 700), forced=((3, 40000),))
     inp = W.make_paged(w, canary=True)
     dev = PagedOnDevice(inp)
     n = 16
     say(f"[parts runs] seqs=45 splits={n}")
     rc, out, _ = dev.run(n)
     assert rc == P.PDA_OK
-    rows = [0, 1, 19, 20, 21, 22, 41, 42, 43, 44]
+    rows = [0, 1, 3, 38, 39, 40, 41, 44]
     sub = W.subset_paged(inp, rows)
     ref, _, _ = A.paged_decode(sub.q, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens,
                                sub.scale)
