@@ -286,17 +286,17 @@ int pda_device_cu_count(int device, uint32_t* cu_count);
  * caches / out 16-byte aligned, workspace 8-byte aligned.  num_seqs == 0
  * launches nothing.
  *
- * Launches with fewer than 128 (KV head, split) pairs per sequence (a long
- * single sequence, small split counts), and non-split launches of the
- * packed kernel, split the work of a sequence over several workgroups that
- * hand partial results to each other through device arrays the library
- * owns (per GPU: 16 MiB of records and 64 Ki counters for each of the two
- * kernels; no allocation; batches beyond them run as several launches).
- * The number of workgroups a sequence uses depends only on the shape, the
- * split count and its own length, so its bytes still do not depend on the
- * batch.  Such calls (this one, pda_splitk_partials and their FP8 forms)
- * must not overlap on one GPU: issue them on one stream, or order the
- * streams.
+ * Launches with fewer than 128 (KV head, split) pairs per sequence split
+ * each split of 129 blocks or more (a long single sequence) over several
+ * workgroups, and non-split launches of the packed kernel split each
+ * sequence of 33 blocks or more over two; the workgroups hand partial
+ * results to each other through device arrays the library owns (per GPU:
+ * 16 MiB of records and 64 Ki counters for each of the two kernels; no
+ * allocation; batches beyond them run as several launches).  The number of
+ * workgroups a sequence uses depends only on the shape, the split count and
+ * its own length, so its bytes still do not depend on the batch.  Such
+ * calls (this one, pda_splitk_partials and their FP8 forms) must not
+ * overlap on one GPU: issue them on one stream, or order the streams.
  * ------------------------------------------------------------------------ */
 int pda_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, const int32_t* seq_lens, void* out,

@@ -33,6 +33,12 @@
 //     state goes to LDS and one fixed-order pass merges them, so the result
 //     depends only on the sequence's own data and the launch shape, never
 //     on the rest of the batch.
+//   * Parts: a long item (a split of a long sequence when a launch gives
+//     each sequence few items, or a long tile of a tiled step) is split
+//     over several workgroups, each folding a contiguous run of its blocks
+//     into an FP32 record; the last to take a ticket combines the records
+//     in part order.  How many parts an item uses depends only on its own
+//     block count, so the bytes still depend only on the sequence's data.
 // Exponentials are v_exp_f32 (base 2): scores are scaled by scale * log2(e)
 // and m is converted back to natural-log units when it is stored.
 #include <hip/hip_runtime.h>
