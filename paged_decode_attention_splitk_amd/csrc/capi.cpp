@@ -193,6 +193,7 @@ hipError_t launch_oneshot(int mode, const DecodeShape& s, int gc, int hg, pda::F
     p.tick = nullptr;
     const uint32_t gx = (uint32_t)(items * parts);
     const uint32_t chunk = parts > 1 ? part_rows(items, parts, gc, s.D) : s.num_seqs;
+    if (chunk == 0) return hipErrorInvalidValue;   // oneshot_parts keeps one row in the arrays
     for (uint32_t r0 = 0; r0 < s.num_seqs; r0 += chunk) {
         const uint32_t rows = s.num_seqs - r0 < chunk ? s.num_seqs - r0 : chunk;
         pda::FoldParams c = p;
