@@ -391,6 +391,32 @@ def main():
     # warm: the same pool every step (K/V partly served from the Infinity Cache)
     warm_ms, _ = timed(lambda i: decode(0))
 
+    # per-step distribution: an event pair around each of K steps (outside
+    # the timed region above; the events add a little to each step)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        decode(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_step = np.sort(np.array([a.elapsed_time(b) * 1e3 for a, b in evs]))
+    pct = lambda q: round(float(np.percentile(per_step, q)), 2)
+
+    # achievable-bandwidth context on this machine: a plain 1 GiB device copy
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9   # read + write
+    del src, dst
+
     value = ab["step"] / (ms_per_step * 1e-3) / 1e9
     # the dominant kernel: the fold (or the packed kernel)
     kern_bytes = ab["fold"]
@@ -423,6 +449,8 @@ def main():
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "gpu_event_us_per_step": round(gpu_ms * 1e3, 2),
         "warm_us_per_step": round(warm_ms * 1e3, 2),
+        "step_us_percentiles": {"p10": pct(10), "p50": pct(50), "p90": pct(90)},
+        "copy_1GiB_GBps": round(copy_gbs, 1),
         "kernels_us": {"splitk_fold": round(fold_avg * 1e3, 2),
                        "splitk_merge": round(merge_avg * 1e3, 2)},
         "roofline": {
