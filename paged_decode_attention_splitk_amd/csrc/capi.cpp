@@ -98,8 +98,9 @@ size_t lds_per_block() {
 }
 
 // Whether a one-shot launch gives each sequence few workgroups (fewer than
-// 128 (KV head, split) items): such launches split every item over several
-// workgroups (oneshot_parts) of PDA_FEW_WAVES waves for a BF16 cache (8:
+// 128 (KV head, split) items): such launches may split a long item over
+// several workgroups (oneshot_parts, grid_parts), and use workgroups of
+// PDA_FEW_WAVES waves for a BF16 cache (8:
 // measured on the 131072-token sequence with 4 parts, fold 53.5 us against
 // 58.4 us at 12 waves and 59.0 at 6) and PDA_FEW_WAVES_FP8 for an FP8 one,
 // within the kernel's limit and the device's LDS per workgroup.
