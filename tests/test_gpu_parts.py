@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 
 import workloads as W
 from oracle import attention as A
-from tests.gpu_util import (PagedOnDevice, ScratchOnDevice, assert_ml_close, assert_out_close,
-                            host_bf16, host_bits, say)
+from tests.gpu_util import (PagedFP8OnDevice, PagedOnDevice, ScratchOnDevice, assert_ml_close,
+                            assert_out_close, host_bf16, host_bits, say)
 
 import paged_decode_attention_splitk_amd as P
 
@@ -180,3 +180,48 @@ def test_part_users_interleaved():
                 assert np.array_equal(host_bits(pd.run(1, packed=True)[1]), base_p), order
             else:
                 assert np.array_equal(host_bits(td.run(64)[0]), base_t), order
+
+
+# More shapes with several parts per item: head dim 64 with 8 heads per KV
+# head (a 40000-token sequence at 4 splits: 5 parts per item), head dim 256
+# with 2 heads per KV head (2 splits: 8 parts), each against the oracle and
+# alone vs co-batched.
+@pytest.mark.parametrize("D,nq,nkv,n", [(64, 16, 2, 4), (256, 8, 4, 2)])
+def test_oneshot_parts_other_shapes(D, nq, nkv, n):
+    w = W.Workload(name=f"parts-d{D}", seed=28, num_seqs=3, num_q_heads=nq, num_kv_heads=nkv,
+                   head_dim=D, block_size=16, seq_lens=(40000, 300, 0))
+    inp = W.make_paged(w, canary=True)
+    dev = PagedOnDevice(inp)
+    say(f"[parts shapes] D={D} nq={nq} nkv={nkv} splits={n}")
+    rc, out, ws = dev.run(n)
+    assert rc == P.PDA_OK
+    ref, _, _ = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                               inp.seq_lens, inp.scale)
+    assert_out_close(host_bf16(out), ref, f"parts D={D}")
+    if n > 1:
+        _partials_close(inp, ws, n)
+    full = host_bits(out)
+    for s in range(3):
+        _, one, _ = dev.run(n, rows=[s])
+        assert np.array_equal(host_bits(one)[0], full[s]), f"seq {s} differs alone (D={D})"
+
+
+def test_oneshot_parts_fp8():
+    """The FP8 fold's parts form: the long-sequence shape with an E4M3 cache
+    and a 40000-token sequence (2 parts per item at 16 splits) against the
+    FP8 oracle, and alone vs co-batched."""
+    from oracle import fp8 as F
+    w = W.Workload(name="parts-fp8", seed=29, num_seqs=3, num_q_heads=24, num_kv_heads=4,
+                   head_dim=128, block_size=16, seq_lens=(40000, 2000, 0))
+    inp = W.make_paged_fp8(w, canary=True)
+    dev = PagedFP8OnDevice(inp)
+    say("[parts fp8] splits=16")
+    rc, out, _ = dev.run(16)
+    assert rc == P.PDA_OK
+    ref = F.paged_decode_fp8(inp.q, inp.k8, inp.v8, inp.block_tables, inp.seq_lens, inp.scale,
+                             inp.k_scale, inp.v_scale)
+    assert_out_close(host_bf16(out), ref, "parts fp8")
+    full = host_bits(out)
+    for s in range(3):
+        _, one, _ = dev.run(16, rows=[s])
+        assert np.array_equal(host_bits(one)[0], full[s]), f"fp8 seq {s} differs alone"
