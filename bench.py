@@ -73,14 +73,68 @@ def load_traffic(per_launch_alg):
     return rec.get("fold_hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, seconds, fp8=False):
-    """The FP64 oracle on the host, one BLAS thread, repeated over the whole
-    batch until `seconds` have passed (at least once)."""
+# Inputs the oracle's worker processes read: set before the pool forks, so
+# every worker inherits them (copy-on-write) instead of receiving a copy.
+_CPU_INP = None
+_CPU_FP8 = False
+
+
+def _oracle_item(item):
+    """One work item of the oracle baseline: the query heads of one (sequence,
+    KV head) for a BF16 cache, or one whole sequence for an FP8 cache (the
+    FP8 oracle works per sequence).  Returns that part of the output."""
+    from oracle import attention as A
+    from oracle import fp8 as F
+    inp = _CPU_INP
+    s, kvh = item
+    if _CPU_FP8:
+        sl = slice(s, s + 1)
+        return F.paged_decode_fp8(inp.q[sl], inp.k8, inp.v8, inp.block_tables[sl],
+                                  inp.seq_lens[sl], inp.scale, inp.k_scale, inp.v_scale)[0]
+    G = inp.q.shape[1] // inp.num_kv_heads
+    heads = [(s, h) for h in range(kvh * G, (kvh + 1) * G)]
+    out, _, _ = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
+                               inp.scale, heads=heads)
+    return out[s, kvh * G:(kvh + 1) * G]
+
+
+def _worker_init():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)   # one BLAS thread per process: the pool supplies the parallelism
+
+
+def cpu_baseline(inp, seconds, fp8=False, single_seconds=5.0, max_workers=16):
+    """The FP64 oracle, unchanged, on the host cores: a pool of processes, one
+    per usable core (at most ``max_workers``), over the batch's (sequence, KV
+    head) items, repeated over the whole batch until ``seconds`` have passed
+    (at least once); then the same oracle on one thread with one BLAS thread,
+    for ``single_seconds``.  Must run before this process touches the GPU:
+    the pool is forked.  Returns a dict of timings and core counts."""
+    import multiprocessing as mp
+
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as A
     from oracle import fp8 as F
-    reps, t0 = 0, time.perf_counter()
+    global _CPU_INP, _CPU_FP8
+    _CPU_INP, _CPU_FP8 = inp, fp8
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(affinity, max_workers))
+    S = inp.q.shape[0]
+    items = [(s, 0) for s in range(S)] if fp8 else \
+        [(s, kvh) for s in range(S) for kvh in range(inp.num_kv_heads)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_worker_init) as pool:
+        pool.map(_oracle_item, items[:workers], chunksize=1)   # workers up and warm
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            pool.map(_oracle_item, items, chunksize=1)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    par_s = el / reps
+    reps1, t0 = 0, time.perf_counter()
     with threadpool_limits(1):
         while True:
             if fp8:
@@ -89,16 +143,18 @@ def cpu_baseline(inp, seconds, fp8=False):
             else:
                 A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
                                inp.seq_lens, inp.scale)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= seconds:
+            reps1 += 1
+            el1 = time.perf_counter() - t0
+            if el1 >= single_seconds:
                 break
-    return el / reps, reps
+    return {"step_s": par_s, "reps": reps, "workers": workers, "items": len(items),
+            "affinity": affinity, "cpu_count": os.cpu_count(),
+            "single_step_s": el1 / reps1, "single_reps": reps1}
 
 
 def tiled_bench(args, K):
     """The tiled state API on the scratch-pool workload: a step is
-    begin_step, every step_tile call of the plan_tiles schedule, finalize.
+    begin_step, every step_tile call of the workloads.plan_tiles schedule, finalize.
     Returns the JSON record (without cpu_baseline)."""
     import numpy as np
     import torch
@@ -110,7 +166,7 @@ def tiled_bench(args, K):
     S, nq, D = sc.q.shape
     nkv, bs, cap = sc.num_kv_heads, sc.block_size, sc.workload.tile_capacity
     lens = sc.seq_lens.astype(np.int64)
-    calls = P.plan_tiles([sc.slot_tables[s] for s in range(S)], [int(x) for x in lens], bs, cap)
+    calls = W.plan_tiles([sc.slot_tables[s] for s in range(S)], [int(x) for x in lens], bs, cap)
     q = torch.from_numpy(np.ascontiguousarray(sc.q).view(np.int16)).cuda()
     pool = torch.from_numpy(np.ascontiguousarray(sc.pool).view(np.int16)).cuda()
     k_ptr = pool.data_ptr()
@@ -266,26 +322,35 @@ def main():
         sys.exit(2)
 
     import numpy as np
+
+    import workloads as W
+
+    layout = W.WORKLOADS[args.workload].layout
+    inp = cpu = None
+    if layout == "paged":
+        inp = (W.make_paged_fp8(args.workload, canary=False) if args.fp8 else
+               W.make_paged(args.workload, canary=False))
+        if not args.no_cpu:
+            # before anything touches the GPU: the oracle's pool is forked
+            cpu = cpu_baseline(inp, args.cpu_seconds, args.fp8)
+
     import torch
 
     import paged_decode_attention_splitk_amd as P
-    import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev_cus = P.pda_device_cu_count(0)
 
-    if W.WORKLOADS[args.workload].layout == "scratch":
+    if layout == "scratch":
         rec = tiled_bench(args, args.steps)
         print(json.dumps(rec), flush=True)
         return
-    if W.WORKLOADS[args.workload].layout == "prefill":
+    if layout == "prefill":
         rec = prefill_bench(args, args.steps)
         print(json.dumps(rec), flush=True)
         return
 
-    inp = (W.make_paged_fp8(args.workload, canary=False) if args.fp8 else
-           W.make_paged(args.workload, canary=False))
     k_host, v_host = (inp.k8, inp.v8) if args.fp8 else (inp.k_cache, inp.v_cache)
     S, nq, D = inp.q.shape
     nkv, bs = inp.num_kv_heads, inp.block_size
@@ -476,16 +541,22 @@ def main():
         tflops = flops / (fold_avg * 1e-3) / 1e12
         rec["mfma"] = {"tflops": round(tflops, 2), "peak_bf16_tflops": 2500.0,
                        "utilisation": round(tflops / 2500.0, 5)}
-    if not args.no_cpu:
-        sec, reps = cpu_baseline(inp, args.cpu_seconds, args.fp8)
+    if cpu is not None:
         rec["cpu_baseline"] = {
-            "value": round(ab["step"] / sec / 1e9, 4),
+            "value": round(ab["step"] / cpu["step_s"] / 1e9, 4),
             "unit": "GB/s",
-            "cores": 1,
+            "cores": cpu["workers"],
             "kind": "oracle",
-            "sample": f"the whole {S}-sequence batch, FP64 numpy oracle with one BLAS thread, "
-                      f"{reps} repetition(s); {sec * 1e3:.1f} ms per step",
-            "ms_per_step": round(sec * 1e3, 2),
+            "sample": f"the whole {S}-sequence batch, FP64 numpy oracle (unchanged) in "
+                      f"{cpu['workers']} processes over {cpu['items']} "
+                      f"{'sequence' if args.fp8 else '(sequence, KV head)'} items, one BLAS "
+                      f"thread each, {cpu['reps']} repetition(s); "
+                      f"{cpu['step_s'] * 1e3:.1f} ms per step",
+            "ms_per_step": round(cpu["step_s"] * 1e3, 2),
+            "os_cpu_count": cpu["cpu_count"],
+            "affinity_cores": cpu["affinity"],
+            "single_thread_ms": round(cpu["single_step_s"] * 1e3, 2),
+            "single_thread_value": round(ab["step"] / cpu["single_step_s"] / 1e9, 4),
         }
     print(json.dumps(rec), flush=True)
 

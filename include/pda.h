@@ -116,8 +116,13 @@ uint64_t pda_workspace_slots(uint64_t rows, uint32_t num_q_heads, uint32_t num_s
 /* 1 iff num_kv_heads > 0, head_dim == 256 and num_q_heads == num_kv_heads * 8
  * (attn_splitk page, module invariants and gqa_pack_shape_ok). */
 int pda_gqa_pack_shape_ok(uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim);
-/* Workgroups of a packed launch: num_kv_heads * num_seqs (attn_splitk page,
- * gqa_pack_ctas). */
+/* Workgroups of a packed launch in the page's shape, one per (sequence, KV
+ * head): num_kv_heads * num_seqs (attn_splitk page, gqa_pack_ctas).  This
+ * library's non-split packed launch (pda_paged_decode with
+ * PDA_DECODE_PACKED and num_splits == 1) may split each (sequence, KV head)
+ * of 33 blocks or more over up to 2 workgroups that combine in-kernel, so
+ * it dispatches up to twice this count; the packed split-K form dispatches
+ * this count times num_splits. */
 uint64_t pda_gqa_pack_ctas(uint32_t num_kv_heads, uint32_t num_seqs);
 /* Tokens per split of one sequence: ceil(seq_len / num_splits) floored at
  * pda_min_kv_per_split(), rounded up to whole blocks.  Split i covers
@@ -254,6 +259,17 @@ int pda_device_cu_count(int device, uint32_t* cu_count);
 /* ------------------------------------------------------------------------
  * One-shot paged decode.
  *
+ * The operation is the problem statement this library answers: one query
+ * per sequence attends softmax(scale * q.K^T).V over its paged cache; the
+ * split-K form follows the "Module attn_splitk" page: its module
+ * description (the KV length of each sequence is cut into num_splits
+ * chunks whose partial states are merged, and because that merge is not
+ * associative the split count must not follow the batch), MAX_DECODE_SPLITS
+ * and workspace_slots (the [o, m, l] partials of every (row, head, split));
+ * the running state (m, l, o unnormalised) and the o / l finalize with 0
+ * where l == 0 follow the "metrale_storage/tiled_attention.rs" page
+ * (module comment, begin_step, finalize).
+ *
  *   q            bf16 [num_seqs, num_q_heads, head_dim]        (device)
  *   k_cache      bf16 [num_blocks, block_size, num_kv_heads, head_dim]
  *   v_cache      bf16, same layout as k_cache
@@ -305,8 +321,13 @@ int pda_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                      uint32_t block_size, uint32_t max_blocks_per_seq, uint32_t num_blocks,
                      float scale, uint32_t num_splits, uint32_t flags, void* stream);
 
-/* The merge pass alone: reads the workspace written by a split-K launch of
- * the same shape and writes out (bf16 [num_seqs, num_q_heads, head_dim]).
+/* The merge pass alone ("Module attn_splitk", module description: the
+ * split partial states of one (row, head) are combined into one output;
+ * workspace_slots for their layout): reads the workspace written by a
+ * split-K launch of the same shape and writes out (bf16 [num_seqs,
+ * num_q_heads, head_dim]): per (row, head), over the splits in index order,
+ * M = max m_i, w_i = exp(m_i - M), out = sum w_i o_i / sum w_i l_i, or 0 when
+ * every split has l == 0.
  * Splits with l == 0 are skipped; their o is never read.  Exposed so the
  * partials can be checked and timed on their own; pda_paged_decode already
  * runs it. */
@@ -314,8 +335,10 @@ int pda_splitk_merge(const float* workspace, uint64_t workspace_floats, void* ou
                      uint32_t num_seqs, uint32_t num_q_heads, uint32_t head_dim,
                      uint32_t num_splits, void* stream);
 
-/* pda_paged_decode without the merge: leaves the partials in the workspace
- * (num_splits >= 2).  flags: PDA_DECODE_UNPACKED or PDA_DECODE_DEFAULT (the
+/* pda_paged_decode without the merge ("Module attn_splitk": the split
+ * partials of workspace_slots, one [o, m, l] slot per (row, head, split)):
+ * leaves the partials in the workspace (num_splits >= 2); o is unnormalised,
+ * m in natural-log units, and an empty split holds m = -inf, l = 0.  flags: PDA_DECODE_UNPACKED or PDA_DECODE_DEFAULT (the
  * split-K fold kernel), or PDA_DECODE_PACKED (the packed MFMA kernel's
  * split-K form; PDA_NOT_APPLICABLE unless pda_gqa_pack_shape_ok). */
 int pda_splitk_partials(const void* q, const void* k_cache, const void* v_cache,

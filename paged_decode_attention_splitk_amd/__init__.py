@@ -429,49 +429,3 @@ class TiledAttention:
 
     def finalize(self, out, num_seqs, stream=None):
         pda_tiled_finalize(self.handle, out, num_seqs, stream)
-
-
-def plan_tiles(block_lists, seq_lens, block_size, tile_capacity):
-    """Schedule whole-sequence KV folding as step_tile calls.
-
-    ``block_lists[s]`` holds sequence s's block ids in token order.  Each
-    call carries, per sequence, up to ``tile_capacity`` of its next blocks
-    and one ``last_block_valid_slots`` value for all of them, so a sequence
-    whose last block is partial gets that block in a call of its own,
-    grouped with the other sequences that end with the same number of valid
-    slots.  Returns a list of (tile_blocks [S][cap] lists, counts [S],
-    last_block_valid_slots).  Pure host logic; nothing is launched.
-    """
-    S = len(seq_lens)
-    full = []      # per sequence: list of blocks that are entirely valid
-    tail = []      # per sequence: (block, valid) of a partial last block, or None
-    for s in range(S):
-        L = int(seq_lens[s])
-        n = -(-L // block_size)
-        blocks = [int(b) for b in block_lists[s][:n]]
-        r = L - (n - 1) * block_size if n else 0
-        if n and r < block_size:
-            full.append(blocks[:-1])
-            tail.append((blocks[-1], r))
-        else:
-            full.append(blocks)
-            tail.append(None)
-    calls = []
-    rounds = max((-(-len(f) // tile_capacity) for f in full), default=0)
-    for i in range(rounds):
-        tb = [[0] * tile_capacity for _ in range(S)]
-        cnt = [0] * S
-        for s in range(S):
-            part = full[s][i * tile_capacity:(i + 1) * tile_capacity]
-            tb[s][:len(part)] = part
-            cnt[s] = len(part)
-        calls.append((tb, cnt, block_size))
-    for r in sorted({t[1] for t in tail if t is not None}):
-        tb = [[0] * tile_capacity for _ in range(S)]
-        cnt = [0] * S
-        for s in range(S):
-            if tail[s] is not None and tail[s][1] == r:
-                tb[s][0] = tail[s][0]
-                cnt[s] = 1
-        calls.append((tb, cnt, r))
-    return calls

@@ -513,7 +513,8 @@ int pda_splitk_partials_fp8(const void* q, const void* k_cache, const void* v_ca
 
 int pda_prefill_applies(uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
                         int causal, uint32_t sliding_window) {
-    return head_dim == 256 && causal && sliding_window == 0 && num_kv_heads > 0 &&
+    return head_dim == pda::kPrefillHeadDim && causal && sliding_window == 0 &&
+           num_kv_heads > 0 &&
            num_q_heads % num_kv_heads == 0;
 }
 

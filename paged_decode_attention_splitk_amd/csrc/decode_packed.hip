@@ -54,6 +54,12 @@ namespace {
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kD = 256;            // packed head dim
 constexpr int kG = 8;              // packed query heads per KV head
+// The kernel is compiled for exactly the shape the host gate dispatches to
+// it ("Module attn_splitk": DECODE_GQA_PACK_WIDTH, DECODE_GQA_PACK_HEAD_DIM,
+// gqa_pack_shape_ok); a change to either side that breaks the match fails
+// the build.
+static_assert(kG == (int)kGqaPackWidth, "packed kernel width differs from the dispatch gate");
+static_assert(kD == (int)kGqaPackHeadDim, "packed kernel head dim differs from the dispatch gate");
 constexpr int kTile = 16;          // tokens per tile
 constexpr int kWaves = 8;          // waves per workgroup, non-split form
 constexpr int kVTileElems = kTile * kD;   // one wave's V tile in LDS (8 KiB)

@@ -24,6 +24,8 @@ constexpr uint32_t kGqaPackWidth = 8;
 constexpr uint32_t kGqaPackHeadDim = 256;
 constexpr uint32_t kMinKvPerSplit = 64;
 constexpr uint32_t kMaxHeadDim = 256;
+// Head dim of the causal prefill kernel (prefill page, applies: head_dim 256).
+constexpr uint32_t kPrefillHeadDim = 256;
 // Block sizes are multiples of this, so a split (which starts on a block)
 // always starts on a token group of the fold loop.
 constexpr uint32_t kBlockQuantum = 16;

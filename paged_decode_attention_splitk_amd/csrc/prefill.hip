@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pda_geometry.h"
 #include "pda_kernels.h"
 
 namespace pda {
@@ -36,6 +37,8 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kD = 256;           // head dim
+// compiled for the head dim the host gate (pda_prefill_applies) accepts
+static_assert(kD == (int)kPrefillHeadDim, "prefill kernel head dim differs from its gate");
 #ifndef PDA_PREFILL_WAVES
 #define PDA_PREFILL_WAVES 8
 #endif

@@ -14,6 +14,7 @@ import numpy as np
 import torch
 
 import paged_decode_attention_splitk_amd as P
+import workloads as W
 
 ATOL_OUT, RTOL_OUT = 1.6e-2, 1e-2
 RTOL_ML = 1e-4
@@ -115,7 +116,7 @@ class ScratchOnDevice:
 
     def run(self, tile_capacity, rows=None, handle=None):
         """Fold the sequences ``rows`` (default: all) through the tiled API
-        with the plan of plan_tiles; returns (out bf16 tensor, m, l, o)."""
+        with the plan of workloads.plan_tiles; returns (out bf16 tensor, m, l, o)."""
         sc = self.sc
         rows = list(range(sc.num_seqs)) if rows is None else list(rows)
         S = len(rows)
@@ -127,7 +128,7 @@ class ScratchOnDevice:
         strides = handle.scratch_pool_strides()
         k_ptr = self.pool.data_ptr()
         v_ptr = k_ptr + self.v_off_bytes
-        calls = P.plan_tiles([sc.slot_tables[s] for s in rows],
+        calls = W.plan_tiles([sc.slot_tables[s] for s in rows],
                              [int(sc.seq_lens[s]) for s in rows], sc.block_size, tile_capacity)
         handle.begin_step(S)
         keep = []

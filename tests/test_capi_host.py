@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import paged_decode_attention_splitk_amd as P
+import workloads as W
 from oracle import geometry as g
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -174,7 +175,7 @@ def test_plan_tiles_covers_every_token_once_in_order(bs, cap):
         n = -(-L // bs)
         tables.append(list(range(nxt, nxt + n)) + [-1] * 3)
         nxt += n
-    calls = P.plan_tiles(tables, lens, bs, cap)
+    calls = W.plan_tiles(tables, lens, bs, cap)
     for tb, cnt, lbvs in calls:
         assert 1 <= lbvs <= bs and all(0 <= c <= cap for c in cnt)
     seen = _fold_plan(calls, len(lens))
@@ -272,3 +273,39 @@ def test_missing_library_fails_loudly(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "no CPU fallback" in r.stdout
+
+
+CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                    "paged_decode_attention_splitk_amd", "csrc")
+
+
+def _constexpr_int(src, name):
+    m = re.search(rf"constexpr\s+int\s+{name}\s*=\s*(\d+)\s*;", src)
+    assert m, f"no 'constexpr int {name} = N;' in the source"
+    return int(m.group(1))
+
+
+def test_kernel_sources_declare_the_dispatched_pack_shape():
+    """The packed kernel is compiled for the width and head dim that the host
+    gate dispatches to it, and says so in a static_assert ("Module
+    attn_splitk": DECODE_GQA_PACK_WIDTH, DECODE_GQA_PACK_HEAD_DIM; the page
+    pins the kernel sources' declared width to the dispatch width with a
+    test).  Likewise the prefill kernel's head dim and its gate."""
+    packed = open(os.path.join(CSRC, "decode_packed.hip")).read()
+    assert _constexpr_int(packed, "kG") == P.pda_gqa_pack_width() == g.DECODE_GQA_PACK_WIDTH
+    assert _constexpr_int(packed, "kD") == P.pda_gqa_pack_head_dim() == 256
+    assert re.search(r"static_assert\(\s*kG\s*==\s*\(int\)kGqaPackWidth", packed)
+    assert re.search(r"static_assert\(\s*kD\s*==\s*\(int\)kGqaPackHeadDim", packed)
+    # the gate admits exactly the compiled shape
+    G, D = _constexpr_int(packed, "kG"), _constexpr_int(packed, "kD")
+    assert P.pda_gqa_pack_shape_ok(4 * G, 4, D)
+    assert not P.pda_gqa_pack_shape_ok(4 * (G + 1), 4, D)
+    assert not P.pda_gqa_pack_shape_ok(4 * G, 4, D // 2)
+    prefill = open(os.path.join(CSRC, "prefill.hip")).read()
+    Dp = _constexpr_int(prefill, "kD")
+    assert re.search(r"static_assert\(\s*kD\s*==\s*\(int\)kPrefillHeadDim", prefill)
+    assert P.pda_prefill_applies(32, 4, Dp)
+    assert not P.pda_prefill_applies(32, 4, Dp // 2)
+    # the fold kernel's widest head group is the pack width
+    kernels = open(os.path.join(CSRC, "pda_kernels.h")).read()
+    assert _constexpr_int(kernels, "kMaxHeadsPerGroup") == P.pda_gqa_pack_width()

@@ -61,18 +61,12 @@ def test_batch_workload_auto_full_size():
     ref, m, l = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
                                inp.seq_lens, inp.scale)
     assert_out_close(host_bf16(out), ref)
-    # workspace m / l of every split on four sequences
-    S, nq, D = inp.num_seqs, inp.num_q_heads, inp.head_dim
-    wsn = ws.cpu().numpy().reshape(S, nq, n, D + 2).astype(np.float64)
-    rows = [0, 7, 19, 31]
-    sub = W.subset_paged(inp, rows)
-    po, pm, pl = A.split_partials(sub.q, sub.k_cache, sub.v_cache, sub.block_tables,
-                                  sub.seq_lens, sub.scale, n)
-    assert_ml_close(wsn[rows][..., D], pm, "workspace m")
-    assert_ml_close(wsn[rows][..., D + 1], pl, "workspace l")
-    # the same call again gives the same bytes
+    # workspace m / l / o of every split of every sequence
+    _check_partials(dev, ws, n)
+    # the same call again gives the same bytes, and so does each row alone
     _, out2, _ = dev.run(n)
     assert np.array_equal(host_bits(out), host_bits(out2))
+    _each_row_alone(dev, host_bits(out), n, "batch")
 
 
 def test_long_sequence_clamped_splits():
@@ -88,17 +82,38 @@ def test_long_sequence_clamped_splits():
     _check_partials(dev, ws, n)
 
 
+_PACKED_REF = {}
+
+
+def _packed_reference(inp):
+    """The oracle's output for every row of the packed workload (computed
+    once per module: about 4 s on the host)."""
+    if "out" not in _PACKED_REF:
+        ref, _, _ = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                                   inp.seq_lens, inp.scale)
+        _PACKED_REF["out"] = ref
+    return _PACKED_REF["out"]
+
+
+def _each_row_alone(dev, full, n, what, **kw):
+    """Every row's output bytes alone equal its bytes in the whole batch."""
+    for s in range(dev.inp.num_seqs):
+        _, one, _ = dev.run(n, rows=[s], **kw)
+        assert np.array_equal(host_bits(one)[0], full[s]), f"{what}: seq {s} differs alone"
+
+
 @pytest.mark.parametrize("n", [1, 16])
 def test_packed_shape_unpacked_path(n):
+    """The unpacked split-K path on the packed workload (64 sequences of
+    1K-8K tokens, 32 q / 4 kv heads, head dim 256): all 64 rows against the
+    oracle, and each row alone vs co-batched."""
     say(f"[packed-shape unpacked] splits={n}")
     inp = W.make_paged("packed", canary=True)
     dev = PagedOnDevice(inp)
     rc, out, ws = dev.run(n)
-    rows = [0, 1, 17, 40, 63]
-    sub = W.subset_paged(inp, rows)
-    ref, _, _ = A.paged_decode(sub.q, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens,
-                               sub.scale)
-    assert_out_close(host_bf16(out)[rows], ref)
+    assert rc == P.PDA_OK
+    assert_out_close(host_bf16(out), _packed_reference(inp), f"unpacked splits={n}")
+    _each_row_alone(dev, host_bits(out), n, f"unpacked splits={n}")
 
 
 @pytest.mark.parametrize("lens", [(1, 1, 1), (0, 5, 0, 16), (15, 16, 17, 63, 64, 65, 1000)])
@@ -211,47 +226,38 @@ def test_packed_mfma_workload():
     dev = PagedOnDevice(inp)
     rc, out, _ = dev.run(1, packed=True)
     assert rc == P.PDA_OK
-    ref, _, _ = A.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
-                               inp.scale)
+    ref = _packed_reference(inp)
     got = host_bf16(out)
     assert_out_close(got, ref, "packed")
     _, out_u, _ = dev.run(1)
     assert_out_close(host_bf16(out_u), ref, "unpacked")
-    # batch invariance of the packed launch
-    full = host_bits(out)
-    for s in (0, 13, 63):
-        _, one, _ = dev.run(1, packed=True, rows=[s])
-        assert np.array_equal(host_bits(one)[0], full[s]), f"packed seq {s} differs alone"
+    # batch invariance of the packed launch, every row
+    _each_row_alone(dev, host_bits(out), 1, "packed", packed=True)
 
 
 def test_packed_split_k_workload():
     """The packed kernel's split-K form (this library's extension) at the Auto
-    split count on the packed workload: sampled rows against the oracle, the
-    workspace m / l of two rows against the oracle's split partials, and
-    batch invariance."""
+    split count on the packed workload: all 64 rows against the oracle, the
+    workspace m / l of every split of every row against the oracle's split
+    partials, and each row alone vs co-batched."""
     inp = W.make_paged("packed", canary=True)
     n = P.pda_auto_splits(CU, inp.num_q_heads)
     say(f"[packed split-K] splits={n}")
     dev = PagedOnDevice(inp)
     rc, out, ws = dev.run(n, packed=True)
     assert rc == P.PDA_OK
-    rows = [0, 1, 17, 40, 63]
-    sub = W.subset_paged(inp, rows)
-    ref, _, _ = A.paged_decode(sub.q, sub.k_cache, sub.v_cache, sub.block_tables, sub.seq_lens,
-                               sub.scale)
-    assert_out_close(host_bf16(out)[rows], ref, "packed split-K")
+    assert_out_close(host_bf16(out), _packed_reference(inp), "packed split-K")
     S, nq, D = inp.num_seqs, inp.num_q_heads, inp.head_dim
     wsn = ws.cpu().numpy().reshape(S, nq, n, D + 2).astype(np.float64)
-    prow = [1, 40]
-    psub = W.subset_paged(inp, prow)
-    po, pm, pl = A.split_partials(psub.q, psub.k_cache, psub.v_cache, psub.block_tables,
-                                  psub.seq_lens, psub.scale, n)
-    assert_ml_close(wsn[prow][..., D], pm, "packed workspace m")
-    assert_ml_close(wsn[prow][..., D + 1], pl, "packed workspace l")
-    full = host_bits(out)
-    for s in (0, 40):
-        _, one, _ = dev.run(n, packed=True, rows=[s])
-        assert np.array_equal(host_bits(one)[0], full[s]), f"packed split-K seq {s} differs alone"
+    say("[packed split-K] oracle split partials, all rows")
+    po, pm, pl = A.split_partials(inp.q, inp.k_cache, inp.v_cache, inp.block_tables,
+                                  inp.seq_lens, inp.scale, n)
+    assert_ml_close(wsn[..., D], pm, "packed workspace m")
+    assert_ml_close(wsn[..., D + 1], pl, "packed workspace l")
+    live = pl > 0
+    assert_out_close(wsn[..., :D][live] / wsn[..., D + 1][live][:, None],
+                     po[live] / pl[live][:, None], "packed workspace o / l")
+    _each_row_alone(dev, host_bits(out), n, "packed split-K", packed=True)
 
 
 @pytest.mark.parametrize("bs", [16, 32])

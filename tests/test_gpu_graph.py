@@ -89,7 +89,7 @@ def test_tiled_step_graph_replays():
     strides = h.scratch_pool_strides()
     k_ptr = dev.pool.data_ptr()
     v_ptr = k_ptr + dev.v_off_bytes
-    calls = P.plan_tiles([sc.slot_tables[s] for s in range(S)],
+    calls = W.plan_tiles([sc.slot_tables[s] for s in range(S)],
                          [int(x) for x in sc.seq_lens], sc.block_size, 64)
     tiles = [(dev_i32(np.array(tb, np.int32).reshape(S, 64)), dev_i32(np.array(cnt, np.int32)),
               lbvs) for tb, cnt, lbvs in calls]
