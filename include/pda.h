@@ -321,6 +321,33 @@ int pda_paged_decode(const void* q, const void* k_cache, const void* v_cache,
                      uint32_t block_size, uint32_t max_blocks_per_seq, uint32_t num_blocks,
                      float scale, uint32_t num_splits, uint32_t flags, void* stream);
 
+/* pda_paged_decode for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without workspace /
+ * workspace_floats, the same kernels and the same output bytes.  The split-K
+ * partials go to a scratch array the library holds in device memory, one per
+ * GPU, 16 MiB (4 Mi FP32 values), for the life of the process.
+ *
+ *   Limit: pda_workspace_slots(num_seqs, num_q_heads, num_splits, head_dim)
+ *   must not exceed 4194304 (the batch decode shape of 32 sequences, 32 q
+ *   heads, head dim 128 at 16 splits needs 2129920); larger calls return
+ *   PDA_EINVAL before anything is launched.  num_splits == 1 uses no
+ *   scratch.  Nothing in the scratch has to start at any value: every slot
+ *   the merge reads is written earlier in the same call.
+ *
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap on
+ * one GPU (different streams, or several threads) race and give undefined
+ * results: issue them on one stream, or order the streams.  The same holds
+ * with pda_paged_decode calls that split items into parts (see above).
+ * Calls no hipMalloc, hipFree or allocating routine; the first call on a
+ * device looks the scratch address up (hipGetSymbolAddress). */
+int pda_paged_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                             uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads,
+                             uint32_t head_dim, uint32_t block_size,
+                             uint32_t max_blocks_per_seq, uint32_t num_blocks, float scale,
+                             uint32_t num_splits, uint32_t flags, void* stream);
+
 /* The merge pass alone ("Module attn_splitk", module description: the
  * split partial states of one (row, head) are combined into one output;
  * workspace_slots for their layout): reads the workspace written by a

@@ -95,6 +95,8 @@ _SIGS = {
     "pda_gqa_pack_enabled": (_int, []),
     "pda_paged_decode": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _u64, _u32, _u32, _u32,
                                 _u32, _u32, _u32, _u32, _f32, _u32, _u32, _vp]),
+    "pda_paged_decode_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _u32, _u32, _u32, _u32,
+                                        _u32, _u32, _u32, _f32, _u32, _u32, _vp]),
     "pda_splitk_merge": (_int, [_vp, _u64, _vp, _u32, _u32, _u32, _u32, _vp]),
     "pda_splitk_partials": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _u64, _u32, _u32, _u32, _u32,
                                    _u32, _u32, _u32, _f32, _u32, _u32, _vp]),
@@ -248,6 +250,16 @@ def pda_paged_decode(q, k_cache, v_cache, block_tables, seq_lens, out, workspace
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), _ptr(out),
         _ptr(workspace), workspace_floats, num_seqs, num_q_heads, num_kv_heads, head_dim,
         block_size, max_blocks_per_seq, num_blocks, scale, num_splits, flags, _stream(stream)))
+
+
+def pda_paged_decode_noalloc(q, k_cache, v_cache, block_tables, seq_lens, out, num_seqs,
+                             num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, num_blocks, scale, num_splits,
+                             flags=PDA_DECODE_UNPACKED, stream=None) -> int:
+    return _check(_lib.pda_paged_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), _ptr(out),
+        num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+        num_blocks, scale, num_splits, flags, _stream(stream)))
 
 
 def pda_splitk_merge(workspace, workspace_floats, out, num_seqs, num_q_heads, head_dim,

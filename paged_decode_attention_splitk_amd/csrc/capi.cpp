@@ -6,7 +6,7 @@
 // begin_step, step_tile, finalize, the public state buffers); "not
 // applicable" for the packed kernel mirrors that page set's convention of a
 // launcher that launches nothing and lets the caller run the other path.
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdarg>
@@ -455,6 +455,34 @@ int decode_impl(const DecodeShape& s, const void* q, const void* k, const void* 
     return ok();
 }
 
+// Workspace of pda_paged_decode_noalloc: a device array of this library,
+// one copy per GPU, which each GPU holds until the process ends.  Its host
+// name is not a device address: host code uses only the address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).
+constexpr uint64_t kNoAllocWorkspaceFloats = 1u << 22;   // 16 MiB
+static __device__ __align__(256) float scratch[kNoAllocWorkspaceFloats];
+
+// Address of `scratch` on the current device, looked up once per device
+// with that device current; *err receives a failing HIP code.
+float* noalloc_scratch(hipError_t* err) {
+    static std::mutex mu;
+    static std::vector<std::pair<int, float*>> cache;
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> g(mu);
+    for (const auto& c : cache)
+        if (c.first == dev) return c.second;
+    void* ptr = nullptr;
+    *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess || !ptr) {
+        if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+        return nullptr;
+    }
+    cache.emplace_back(dev, static_cast<float*>(ptr));
+    return static_cast<float*>(ptr);
+}
+
 }  // namespace
 
 extern "C" {
@@ -596,6 +624,36 @@ int pda_paged_decode(const void* q, const void* k_cache, const void* v_cache,
     return decode_impl(s, q, k_cache, v_cache, block_tables, seq_lens, out, workspace,
                        workspace_floats, scale, num_splits, flags, (hipStream_t)stream,
                        kBf16Kv);
+}
+
+int pda_paged_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                             uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads,
+                             uint32_t head_dim, uint32_t block_size,
+                             uint32_t max_blocks_per_seq, uint32_t num_blocks, float scale,
+                             uint32_t num_splits, uint32_t flags, void* stream) {
+    const DecodeShape s{num_seqs, num_q_heads, num_kv_heads, head_dim,
+                        block_size, max_blocks_per_seq, num_blocks};
+    // every argument check runs before the scratch lookup (the first HIP call)
+    int rc = check_decode(s, q, k_cache, v_cache, block_tables, seq_lens, out, true);
+    if (rc != PDA_OK) return rc;
+    if (num_splits < 1 || num_splits > pda::kMaxDecodeSplits)
+        return fail(PDA_EINVAL, "num_splits %u outside 1..%u", num_splits, pda::kMaxDecodeSplits);
+    const uint64_t need =
+        num_splits > 1 ? pda_workspace_slots(num_seqs, num_q_heads, num_splits, head_dim) : 0;
+    if (need > kNoAllocWorkspaceFloats)
+        return fail(PDA_EINVAL,
+                    "the split-K workspace needs %llu floats; pda_paged_decode_noalloc holds "
+                    "%llu (pass a workspace to pda_paged_decode instead)",
+                    (unsigned long long)need, (unsigned long long)kNoAllocWorkspaceFloats);
+    float* ws = nullptr;
+    if (need > 0 && num_seqs > 0) {
+        hipError_t e = hipSuccess;
+        ws = noalloc_scratch(&e);
+        if (!ws) return hip_fail(e, "hipGetSymbolAddress (scratch workspace)");
+    }
+    return decode_impl(s, q, k_cache, v_cache, block_tables, seq_lens, out, ws, need, scale,
+                       num_splits, flags, (hipStream_t)stream, kBf16Kv);
 }
 
 // ---------------------------------------------------------------------------

@@ -309,3 +309,28 @@ def test_kernel_sources_declare_the_dispatched_pack_shape():
     # the fold kernel's widest head group is the pack width
     kernels = open(os.path.join(CSRC, "pda_kernels.h")).read()
     assert _constexpr_int(kernels, "kMaxHeadsPerGroup") == P.pda_gqa_pack_width()
+
+
+def _noalloc(**kw):
+    a = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, block_tables=FAKE, seq_lens=FAKE, out=FAKE,
+             num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+             max_blocks_per_seq=8, num_blocks=32, scale=0.1, num_splits=4, flags=0, stream=0)
+    a.update(kw)
+    return P.pda_paged_decode_noalloc(**a)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(num_kv_heads=0), dict(head_dim=96), dict(block_size=8), dict(num_splits=0),
+    dict(num_splits=17), dict(q=None), dict(out=None), dict(k_cache=FAKE + 2),
+    # 64 x 32 heads x 16 splits x (128 + 2) floats is past the 4 Mi-float scratch
+    dict(num_seqs=64, num_q_heads=32, num_kv_heads=8, num_splits=16),
+])
+def test_noalloc_rejects_bad_arguments_before_any_hip_call(bad):
+    with pytest.raises(P.PdaError) as e:
+        _noalloc(**bad)
+    assert e.value.code == P.PDA_EINVAL
+    assert P.pda_last_error()
+
+
+def test_noalloc_empty_batch_is_a_no_op():
+    assert _noalloc(num_seqs=0) == P.PDA_OK
