@@ -206,6 +206,32 @@ def tiled_bench(args, K):
 
     gpu_ms, ms_per_step = timed(step)
     tiles_ms, _ = timed(tiles)
+
+    # the same step captured once in a HIP graph and replayed (the library
+    # launches kernels only, so the step captures as a whole)
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap_stream):
+        cs = cap_stream.cuda_stream
+        h.begin_step(S, stream=cs)
+        for tb, cnt, lbvs in dev_calls:
+            h.step_tile(q, k_ptr, v_ptr, sc.num_slots, tb, cnt, S, strides, lbvs, stream=cs)
+        h.finalize(out, S, stream=cs)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    g0.record(stream)
+    for _ in range(K):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_wall_ms = (time.perf_counter() - t0) * 1e3 / K
+    graph_ms = g0.elapsed_time(g1) / K
     # algorithmic bytes: valid K/V once; per active (call, sequence) its q,
     # its tile-table entries and a read + write of its (m, l, o) state; the
     # fill pass writes the state, finalize reads l, o and writes out
@@ -232,6 +258,8 @@ def tiled_bench(args, K):
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "gpu_event_us_per_step": round(gpu_ms * 1e3, 2),
+        "graph_replay_us_per_step": round(graph_wall_ms * 1e3, 2),
+        "graph_replay_gpu_event_us_per_step": round(graph_ms * 1e3, 2),
         "kernels_us": {"step_tile_all_calls": round(tiles_ms * 1e3, 2)},
         "roofline": {"kernel": f"tiled fold (fold_kernel<2,{D},{min(nq // nkv, 8)}>), all calls",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -89,7 +89,10 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 // copy), so handing them over needs no L2 writeback or invalidate: a writer
 // waits for its record stores to complete before its workgroup takes a
 // ticket, and the combining workgroup loads the records only after taking
-// the last ticket.
+// the last ticket.  This relies on the hardware's ordering of those
+// operations rather than on a release / acquire pair (PDA_PARTS_ORDER in
+// pda_kernels.h states the argument and the measured cost of the formal
+// forms).
 __device__ __forceinline__ void put_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -383,6 +386,32 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
         t_begin = f_begin;
     }
 
+    // A tiled launch without parts joins the running state in its epilogue:
+    // that state is requested here, so its loads overlap the fold instead of
+    // following it (two memory round trips fewer per call; the calls that
+    // fold one partial block per sequence are mostly such latency).  The
+    // parts form keeps its registers for the fold loop.
+    float pre_m = kNegInf, pre_l = 0.f;
+    float2 pre_o[2] = {make_float2(0.f, 0.f), make_float2(0.f, 0.f)};
+    if constexpr (MODE == kModeTiled && !PARTS) {
+        {
+            const int64_t rq = (int64_t)seq * p.nq + h0;
+            if (tid < gcount) {
+                pre_m = p.ws[rq + tid];
+                pre_l = p.l_state[rq + tid];
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int i = tid + j * (int)blockDim.x;
+                if (i < gcount * (D / 2)) {
+                    const int h = i / (D / 2);
+                    const int d = (i - h * (D / 2)) * 2;
+                    pre_o[j] = *reinterpret_cast<const float2*>(p.o_state + (rq + h) * D + d);
+                }
+            }
+        }
+    }
+
     // a live range starts on a block (hence group) boundary; an empty split
     // or part starts at the range end, which need not be aligned: it folds
     // nothing
@@ -668,8 +697,8 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
         const int h = tid;
         float M = kNegInf, m_old = kNegInf, m2_old = kNegInf, l_old = 0.f;
         if (with_old) {
-            m_old = p.ws[row_q + h];
-            l_old = p.l_state[row_q + h];
+            m_old = PARTS ? p.ws[row_q + h] : pre_m;
+            l_old = PARTS ? p.l_state[row_q + h] : pre_l;
             m2_old = m_old * kLog2e;
             M = m2_old;
         }
@@ -722,13 +751,16 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
 
     // Per (head, pair of dims): o of every contributor, in a fixed order.
     const int nitems = gcount * (D / 2);
-    for (int i = tid; i < nitems; i += blockDim.x) {
+    for (int i = tid, j = 0; i < nitems; i += blockDim.x, ++j) {
         const int h = i / (D / 2);
         const int d = (i - h * (D / 2)) * 2;
         float o0 = 0.f, o1 = 0.f;
         const int64_t qs = row_q + h;
         if (with_old) {
-            const float2 prev = *reinterpret_cast<const float2*>(p.o_state + qs * D + d);
+            const float2 prev =
+                !PARTS && j == 0   ? pre_o[0]
+                : !PARTS && j == 1 ? pre_o[1]
+                                   : *reinterpret_cast<const float2*>(p.o_state + qs * D + d);
             const float wo = ew[NC * GC + h];
             o0 = wo * prev.x;
             o1 = wo * prev.y;
@@ -767,9 +799,13 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
         __builtin_amdgcn_s_waitcnt(0);   // this thread's record stores are complete
         __syncthreads();
         if (tid == 0)
-            *eT = __hip_atomic_fetch_add(tick, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *eT = PDA_PARTS_ORDER == 1
+                      ? __hip_atomic_fetch_add(tick, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT)
+                      : __hip_atomic_fetch_add(tick, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (*eT != (uint32_t)(P - 1)) return;
+        // the records are read only after this point
+        if (PDA_PARTS_ORDER >= 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (tid == 0) __hip_atomic_store(tick, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const float* const recs = psub + item * PL * REC;
         // weights: ew[i * GC + h] for part i, ew[P * GC + h] for the state

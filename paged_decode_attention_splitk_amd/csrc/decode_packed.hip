@@ -473,9 +473,13 @@ __global__ __launch_bounds__(64 * W, 2) void packed_kernel(const PackedParams p)
         __builtin_amdgcn_s_waitcnt(0);   // this thread's record stores are complete
         __syncthreads();
         if (tid == 0)
-            *eT = __hip_atomic_fetch_add(tick, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *eT = PDA_PARTS_ORDER == 1
+                      ? __hip_atomic_fetch_add(tick, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT)
+                      : __hip_atomic_fetch_add(tick, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (*eT != (uint32_t)(P - 1)) return;
+        // the records are read only after this point
+        if (PDA_PARTS_ORDER >= 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (tid == 0) __hip_atomic_store(tick, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const float* const recs = g_packed_sub + item * PL * kPackedRec;
         float* const cw = reinterpret_cast<float*>(smem) + 4;   // weights [part][head]

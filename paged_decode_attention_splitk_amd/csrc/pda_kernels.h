@@ -47,6 +47,24 @@ struct FoldParams {
     uint32_t* tick;          // [item] arrival counters, 0 between launches
 };
 
+// Ordering of the part hand-over (record stores, ticket, record loads).
+// 0 (default): every record store is an agent-scope atomic store (it writes
+// through the XCD's non-coherent L2), each thread waits for its stores to
+// be acknowledged (s_waitcnt 0) before the workgroup barrier, one thread
+// then takes the ticket with a relaxed agent-scope atomic (performed at the
+// device-coherent level), and the combining workgroup reads the records
+// with agent-scope atomic loads issued only after the ticket value has
+// come back through LDS and a barrier (the barrier's workgroup fences keep
+// the compiler from moving the loads above it).  Correctness rests on that
+// hardware ordering, not on a release / acquire pair of the memory model.
+// 1: the ticket is an agent-scope acquire-release RMW and the combiner
+// fences (acquire); 2: the combiner alone fences (acquire).  Both are
+// formally ordered and measured slower on MI355X (L2 writeback /
+// invalidate per workgroup): the 131072-token sequence +14 % / +12 %, the
+// packed batch +12 % / +2.4 %, the tiled step +32 % / +5 %.
+#ifndef PDA_PARTS_ORDER
+#define PDA_PARTS_ORDER 0
+#endif
 // Heads one fold workgroup carries at most (the packed width).
 constexpr int kMaxHeadsPerGroup = 8;
 

@@ -535,14 +535,30 @@ def plan_tiles(block_lists, seq_lens, block_size, tile_capacity):
             full.append(blocks)
             tail.append(None)
     calls = []
-    rounds = max((-(-len(f) // tile_capacity) for f in full), default=0)
+    # tiles of a sequence: its full blocks cut every tile_capacity blocks from
+    # the start (the same cut alone or in any batch)
+    tiles = [[f[i:i + tile_capacity] for i in range(0, len(f), tile_capacity)] for f in full]
+    rounds = max((len(t) for t in tiles), default=0)
+    # each sequence's tiles go, in order, to the rounds that hold the fewest
+    # blocks so far (sequences with more tiles placed first), so every round
+    # carries about the same work; a sequence's tiles and their order do not
+    # depend on the rest of the batch, only the round numbers do
+    load = [0] * rounds
+    slot = [[] for _ in range(S)]
+    for s in sorted(range(S), key=lambda s: (-len(tiles[s]), -len(full[s]), s)):
+        k = len(tiles[s])
+        pick = sorted(sorted(range(rounds), key=lambda r: (load[r], r))[:k])
+        for r, t in zip(pick, tiles[s]):
+            load[r] += len(t)
+        slot[s] = pick
     for i in range(rounds):
         tb = [[0] * tile_capacity for _ in range(S)]
         cnt = [0] * S
         for s in range(S):
-            part = full[s][i * tile_capacity:(i + 1) * tile_capacity]
-            tb[s][:len(part)] = part
-            cnt[s] = len(part)
+            if i in slot[s]:
+                part = tiles[s][slot[s].index(i)]
+                tb[s][:len(part)] = part
+                cnt[s] = len(part)
         calls.append((tb, cnt, block_size))
     for r in sorted({t[1] for t in tail if t is not None}):
         tb = [[0] * tile_capacity for _ in range(S)]
