@@ -51,6 +51,7 @@ constexpr int kKT = 32;           // keys per staged tile (two 16-key blocks)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileElems = kKT * kD;          // one K (or V) tile: 16 KiB
 constexpr int kChunksPerThread = kKT * (kD / 8) / kThreads;   // 16-byte pieces
+static_assert(kChunksPerThread * kThreads == kKT * (kD / 8), "threads divide a tile's pieces");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -135,24 +136,43 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     for (int nb = 0; nb < 16; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = kNegInf, l = 0.f;   // of query c (same in all four groups)
 
-    // staging: thread t moves 16-byte pieces t + kThreads * i of the tile
-    // (row = idx / 32, piece = idx % 32) for K and for V
     const uint16_t* kbase = p.k + (int64_t)kvh * kD;
     const uint16_t* vbase = p.v + (int64_t)kvh * kD;
+    // the pool row of key j, or of key 0 for a key past the cache or in a
+    // block outside the pool (its scores are masked); bj = table entry of
+    // key j's block (read for key 0 past the cache), b0 = table entry 0
+    auto key_row = [&](int j, int bj, int b0) -> int64_t {
+        const bool ok = j < p.kv_len && (uint32_t)bj < p.num_blocks;
+        const int blk = ok ? bj : ((uint32_t)b0 < p.num_blocks ? b0 : 0);   // (any in-pool block)
+        return (int64_t)blk * p.blk_s + (int64_t)((ok ? j : 0) % p.bs) * p.tok_s;
+    };
+    // staging: thread t moves 16-byte pieces t + kThreads * i of the tile
+    // (row = idx / 32, piece = idx % 32) for K and for V
     typedef u32x4_t Stage[2][kChunksPerThread];   // K, V pieces of one tile
-    auto stage_load = [&](int tile, Stage& st) {
+    // Table entries.  With a block size that is a multiple of 16, the 16
+    // rows a thread's piece i lies in (rows 16 i .. 16 i + 15 of the tile)
+    // sit in one block, since tiles start on a multiple of 32, so those
+    // entries are the same for the whole workgroup: they are read one tile
+    // ahead of the loads that use them (key kv_len - 1 stands in past the
+    // cache).  Other block sizes read each piece's entry with the tile's
+    // loads, every table read of the tile first, with no branch between
+    // them, so they are waited for once.
+    static_assert(kThreads == 512 && kChunksPerThread == 2, "piece i covers rows 16 i .. 16 i + 15");
+    const bool uniform_tbl = p.bs % 16 == 0;
+    auto tbl_half = [&](int tile, int i) {
+        return uniform_tbl ? p.table[min(tile * kKT + 16 * i, p.kv_len - 1) / p.bs] : 0;
+    };
+    const int b0 = p.table[0];
+    auto stage_load = [&](int tile, Stage& st, const int (&bt)[2]) {
+        int jr[kChunksPerThread], bj[kChunksPerThread];
 #pragma unroll
         for (int i = 0; i < kChunksPerThread; ++i) {
-            const int idx = tid + kThreads * i;
-            const int row = idx >> 5, piece = idx & 31;
-            int j = tile * kKT + row;
-            int blk = j < p.kv_len ? p.table[j / p.bs] : -1;
-            if ((uint32_t)blk >= p.num_blocks) {   // past the cache or dropped: key 0
-                j = 0;
-                blk = p.table[0];
-                if ((uint32_t)blk >= p.num_blocks) blk = 0;   // (any in-pool block)
-            }
-            const int64_t off = (int64_t)blk * p.blk_s + (int64_t)(j % p.bs) * p.tok_s + piece * 8;
+            jr[i] = tile * kKT + ((tid + kThreads * i) >> 5);
+            bj[i] = uniform_tbl ? bt[i] : p.table[(jr[i] < p.kv_len ? jr[i] : 0) / p.bs];
+        }
+#pragma unroll
+        for (int i = 0; i < kChunksPerThread; ++i) {
+            const int64_t off = key_row(jr[i], bj[i], b0) + ((tid + kThreads * i) & 31) * 8;
             st[0][i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
             st[1][i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
         }
@@ -171,10 +191,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     };
     Stage ra, rb;   // tile j's pieces live in (j even ? ra : rb) from load to store
 
+    int tb[2] = {0, 0};   // table entries of the next tile to load
     if (n_tiles > 0) {
-        stage_load(0, ra);
+        const int t0[2] = {tbl_half(0, 0), tbl_half(0, 1)};
+        stage_load(0, ra, t0);
         stage_store(0, ra);
-        if (n_tiles > 1) stage_load(1, rb);
+        if (n_tiles > 1) {
+            const int t1[2] = {tbl_half(1, 0), tbl_half(1, 1)};
+            stage_load(1, rb, t1);
+        }
+        if (n_tiles > 2) {
+            tb[0] = tbl_half(2, 0);
+            tb[1] = tbl_half(2, 1);
+        }
     }
     __syncthreads();
 
@@ -182,7 +211,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     // tile t computes, tile t + 1 (loaded an iteration earlier) goes to LDS
     auto body = [&](int t, Stage& cur, Stage& nxt) {
         const int buf = t & 1;
-        if (t + 2 < n_tiles) stage_load(t + 2, cur);
+        if (t + 2 < n_tiles) stage_load(t + 2, cur, tb);
+        if (t + 3 < n_tiles) {
+            tb[0] = tbl_half(t + 3, 0);
+            tb[1] = tbl_half(t + 3, 1);
+        }
         const uint16_t* kt = smem + buf * 2 * kTileElems;
         const uint16_t* vt = kt + kTileElems;
         const int key0 = t * kKT;
@@ -190,19 +223,49 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
         // row of this wave, or past the cache
         if (key0 <= wave_last_pos && key0 < p.kv_len) {
             const bool live1 = key0 + 16 <= wave_last_pos && key0 + 16 < p.kv_len;
-            // S^T = K . Q^T over the 256 dims, both 16-key blocks interleaved
+            // S^T = K . Q^T over the 256 dims, both 16-key blocks interleaved.
+            // Every K fragment of the tile is requested before the first
+            // MFMA, each into registers of its own, so the LDS reads overlap
+            // one another instead of each waiting for the MFMA before it.
             f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+            bf16x8_t ka0[8], ka1[8];
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) {
-                const bf16x8_t ka0 = __builtin_bit_cast(
+            for (int kb = 0; kb < 8; ++kb)
+                ka0[kb] = __builtin_bit_cast(
                     bf16x8_t, *reinterpret_cast<const u32x4_t*>(kt + kpiece(c, 4 * kb + g)));
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qb[kb], acc0, 0, 0, 0);
-                if (live1) {
-                    const bf16x8_t ka1 = __builtin_bit_cast(
+            if (live1) {
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb)
+                    ka1[kb] = __builtin_bit_cast(
                         bf16x8_t,
                         *reinterpret_cast<const u32x4_t*>(kt + kpiece(16 + c, 4 * kb + g)));
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qb[kb], acc1, 0, 0, 0);
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) {
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[kb], qb[kb], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[kb], qb[kb], acc1, 0, 0, 0);
                 }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb)
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[kb], qb[kb], acc0, 0, 0, 0);
+            }
+            // V fragments of the first 8 dim blocks, requested now (they do
+            // not depend on P), so their LDS reads overlap the softmax: the
+            // transposed reads of the two 16-key blocks (lane c of group g
+            // addresses row 4g + c/4, chunk 4 nb + c%4) give keys 4g .. 4g + 3
+            // of each, in the k order of P below
+            typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_p;
+            const int trow = 4 * g + (c >> 2);
+            auto vread = [&](int nb, int blk) {
+                const uint16_t* src = vt + vchunk(trow, 4 * nb + (c & 3)) + blk * 16 * kD;
+                return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_p)(__attribute__((address_space(3))) uint16_t*)src);
+            };
+            s16x4_t vv0[8], vv1[8];
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                vv0[nb] = vread(nb, 0);
+                vv1[nb] = vread(nb, 1);
             }
             // one softmax step over the tile's 32 keys; acc_b[r]: key
             // key0 + 16 b + 4g + r, query c
@@ -242,22 +305,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
                     for (int nb = 0; nb < 16; ++nb) O[nb][r] *= a;
                 }
             }
-            // O += P . V with the same k order on the B side: the transposed
-            // reads of the two blocks (lane c of group g addresses row
-            // 4g + c/4, chunk 4 nb + c%4) give keys 4g .. 4g + 3 of each
-            const int trow = 4 * g + (c >> 2);
+            // O += P . V with the same k order on the B side; the second 8
+            // dim blocks' fragments are requested as the first 8 are used
 #pragma unroll
-            for (int nb = 0; nb < 16; ++nb) {
-                typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_p;
-                const uint16_t* src0 = vt + vchunk(trow, 4 * nb + (c & 3));
-                const uint16_t* src1 = src0 + 16 * kD;
-                const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_p)(__attribute__((address_space(3))) uint16_t*)src0);
-                const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4_p)(__attribute__((address_space(3))) uint16_t*)src1);
-                const bf16x8_t vb =
-                    __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            for (int nb = 0; nb < 8; ++nb) {
+                const bf16x8_t vb = __builtin_bit_cast(
+                    bf16x8_t, __builtin_shufflevector(vv0[nb], vv1[nb], 0, 1, 2, 3, 4, 5, 6, 7));
                 O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, O[nb], 0, 0, 0);
+                vv0[nb] = vread(nb + 8, 0);
+                vv1[nb] = vread(nb + 8, 1);
+            }
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const bf16x8_t vb = __builtin_bit_cast(
+                    bf16x8_t, __builtin_shufflevector(vv0[nb], vv1[nb], 0, 1, 2, 3, 4, 5, 6, 7));
+                O[nb + 8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, O[nb + 8], 0, 0, 0);
             }
         }
         if (t + 1 < n_tiles) stage_store(buf ^ 1, nxt);
