@@ -31,8 +31,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 CU_COUNT = 256                 # the workloads are stated for 256 compute units
 METRIC = "decode-attention µs/step + achieved HBM GB/s (% of MI355X peak), 32 seqs × 4K ctx"
-FOLD_SRC = os.path.join(ROOT, "paged_decode_attention_splitk_amd", "csrc", "decode_fold.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fold_batch_traffic.json")
+CSRC = os.path.join(ROOT, "paged_decode_attention_splitk_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def alg_bytes(inp, n_splits, kv_elem=2):
@@ -61,16 +61,39 @@ def _src_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def load_traffic(per_launch_alg):
-    """HBM bytes per fold launch from the committed counter summary, or None
-    when missing or taken from a different kernel source."""
+def load_traffic(profile, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/<profile>_traffic.json (rocprofv3 FETCH_SIZE / WRITE_SIZE,
+    copy-calibrated), or None when missing or taken from a different kernel
+    source than the one built here."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(os.path.join(PROFILES, f"{profile}_traffic.json")))
     except (OSError, ValueError):
         return None
-    if rec.get("fold_source_sha256_16") != _src_hash(FOLD_SRC):
+    if rec.get("source_sha256_16") != _src_hash(os.path.join(CSRC, rec.get("source_file", ""))):
         return None
-    return rec.get("fold_hbm_bytes_per_launch")
+    if kernel is None:
+        return (rec.get("per_step") or {}).get("fold_hbm_bytes_per_step")
+    return (rec.get("kernels", {}).get(kernel) or {}).get("hbm_bytes_per_launch")
+
+
+def profile_of(args, n):
+    """(profile name, kernel) of the committed counter summary for the
+    kernel a paged bench leg reports, or (None, None) for other settings."""
+    fp8 = "true" if args.fp8 else "false"
+    if args.workload == "batch" and not args.packed and n == 16:
+        return ("fold_fp8_batch" if args.fp8 else "fold_batch",
+                f"fold_kernel<0, 128, 4, {fp8}, false>")
+    if args.workload == "long" and not args.packed and n == 16:
+        return ("long_fp8" if args.fp8 else "long", f"fold_kernel<0, 128, 6, {fp8}, true>")
+    if args.workload == "packed" and args.packed and n == 1:
+        return ("packed_fp8_nosplit" if args.fp8 else "packed_nosplit",
+                f"packed_kernel<false, 8, {fp8}, true>")
+    if args.workload == "packed" and args.packed and n == 16 and not args.fp8:
+        return "packed_splitk16", "packed_kernel<true, 2, false, false>"
+    if args.workload == "packed" and not args.packed and n == 16 and not args.fp8:
+        return "unpacked_auto16", "fold_kernel<0, 256, 8, false, false>"
+    return None, None
 
 
 # Inputs the oracle's worker processes read: set before the pool forks, so
@@ -152,6 +175,18 @@ def cpu_baseline(inp, seconds, fp8=False, single_seconds=5.0, max_workers=16):
             "single_step_s": el1 / reps1, "single_reps": reps1}
 
 
+def calibrate_copy():
+    """Three plain 1 GiB device-to-device copies: what a counter reads for
+    them scales the same counter of the kernels in a counter run."""
+    import torch
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")   # 1 GiB
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def tiled_bench(args, K):
     """The tiled state API on the scratch-pool workload: a step is
     begin_step, every step_tile call of the workloads.plan_tiles schedule, finalize.
@@ -188,9 +223,16 @@ def tiled_bench(args, K):
         tiles()
         h.finalize(out, S, stream=sp)
 
+    if args.calibrate_copy:
+        calibrate_copy()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        return {"profile_steps": args.profile_steps, "workload": args.workload}
 
     def timed(fn):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -264,7 +306,8 @@ def tiled_bench(args, K):
         "roofline": {"kernel": f"tiled fold (fold_kernel<2,{D},{min(nq // nkv, 8)}>), all calls",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_step": tiles_b},
+                     "traffic": load_traffic("tiled", None),
+                     "algorithmic_bytes_per_step": tiles_b},
     }
 
 
@@ -293,9 +336,16 @@ def prefill_bench(args, K):
                                  len(pi.block_table), pi.num_blocks, pi.scale, stream=sp)
         assert rc == P.PDA_OK
 
+    if args.calibrate_copy:
+        calibrate_copy()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.profile_steps:
+        for _ in range(args.profile_steps):
+            step()
+        torch.cuda.synchronize()
+        return {"profile_steps": args.profile_steps, "workload": args.workload}
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -321,7 +371,9 @@ def prefill_bench(args, K):
         "us_per_step": round(ms * 1e3, 2), "gpu_event_us_per_step": round(gpu_ms * 1e3, 2),
         "roofline": {"kernel": "causal prefill (prefill_kernel)", "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "frac": round(tflops / 2500.0, 4),
+                     "traffic": load_traffic("prefill_4096" if args.workload == "prefill"
+                                             else args.workload, "prefill_kernel"),
                      "kv_bytes_per_step": kv_bytes},
     }
 
@@ -342,6 +394,9 @@ def main():
                     help="FP8 (E4M3) KV cache of the same shape (pda_*_fp8 entry points)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="for counter runs: only the warm-up and this many steps (every "
+                         "one on a cold KV copy), then a short JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -446,12 +501,18 @@ def main():
         assert rc == P.PDA_OK
 
     if args.calibrate_copy:
-        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")   # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+        calibrate_copy()
+
+    if args.profile_steps:
+        for i in range(args.warmup):
+            decode(i)
+        for i in range(args.profile_steps):
+            decode(args.warmup + i)
         torch.cuda.synchronize()
-        del src, dst
+        print(json.dumps({"profile_steps": args.profile_steps, "workload": args.workload,
+                          "kv_pool_copies": copies, "packed": args.packed, "fp8": args.fp8,
+                          "num_splits": n}), flush=True)
+        return
 
     for i in range(args.warmup):
         decode(i)
@@ -511,11 +572,12 @@ def main():
     del src, dst
 
     value = ab["step"] / (ms_per_step * 1e-3) / 1e9
-    # the dominant kernel: the fold (or the packed kernel)
-    kern_bytes = ab["fold"]
+    # the dominant kernel: the fold (or the packed kernel); with one split it
+    # also writes the output itself
+    kern_bytes = ab["fold"] + (ab["merge"] if n == 1 else 0)
     achieved = kern_bytes / (fold_avg * 1e-3) / 1e9
-    traffic = (None if (args.packed or args.fp8 or args.workload != "batch")
-               else load_traffic(kern_bytes))
+    profile, kernel = profile_of(args, n)
+    traffic = load_traffic(profile, kernel) if profile else None
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -547,18 +609,18 @@ def main():
         "kernels_us": {"splitk_fold": round(fold_avg * 1e3, 2),
                        "splitk_merge": round(merge_avg * 1e3, 2)},
         "roofline": {
-            "kernel": (f"GQA-packed MFMA decode (packed_kernel<{'true' if n > 1 else 'false'}, W, "
-                       f"{'true' if args.fp8 else 'false'}>)"
-                       if args.packed else
-                       # parts: launches with fewer than 128 (KV head, split) items per sequence
-                       f"fold (fold_kernel<{0 if n > 1 else 1},{D},{min(nq // nkv, 8)},"
-                       f"{'true' if args.fp8 else 'false'},{'true' if nkv * n < 128 else 'false'}>)"),
+            "kernel": kernel or ("GQA-packed MFMA decode (packed_kernel)" if args.packed
+                                 else "split-K fold (fold_kernel)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "traffic_from": (f"profiles/{profile}_traffic.json: rocprofv3 FETCH_SIZE and "
+                             "WRITE_SIZE of cold dispatches in their own runs, scaled by a "
+                             "1 GiB device copy; not measured in this run"
+                             if traffic is not None else None),
             "algorithmic_bytes_per_launch": kern_bytes,
         },
     }
