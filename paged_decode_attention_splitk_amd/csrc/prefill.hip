@@ -45,6 +45,10 @@ static_assert(kD == (int)kPrefillHeadDim, "prefill kernel head dim differs from 
 constexpr int kWaves = PDA_PREFILL_WAVES;   // 16 query rows each
 constexpr int kRows = 16 * kWaves;          // query rows per workgroup
 constexpr int kKT = 32;           // keys per staged tile (two 16-key blocks)
+#ifndef PDA_PREFILL_LAZY
+#define PDA_PREFILL_LAZY 8
+#endif
+constexpr float kLazy = PDA_PREFILL_LAZY;   // running-max slack, log2 units (p <= 2^kLazy)
 #ifndef PDA_PREFILL_XCD
 #define PDA_PREFILL_XCD 1
 #endif
@@ -121,6 +125,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     const int qrow = min(wr0 + c, p.q_len - 1);     // the query row of lane c
     const int qpos = p.q_offset + wr0 + c;          // its position
     const int wave_last_pos = p.q_offset + wr0 + 15;
+    const int wave_first_pos = p.q_offset + wr0;
     const int64_t row_s = (int64_t)p.nq * kD;       // elements between query rows
 
     // Q as the B operand: lane = query c, 8 dims 32 kb + 8 g of k-step kb
@@ -270,20 +275,34 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
             // one softmax step over the tile's 32 keys; acc_b[r]: key
             // key0 + 16 b + 4g + r, query c
             float s[8];
+            if (key0 + kKT - 1 <= wave_first_pos && key0 + kKT <= p.kv_len) {
+                // every key of the tile is visible to every row of the wave
+                // (so both 16-key blocks were computed)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int k0 = key0 + 4 * g + r, k1 = k0 + 16;
-                s[r] = k0 <= qpos && k0 < p.kv_len ? acc0[r] * p.c : kNegInf;
-                s[4 + r] = live1 && k1 <= qpos && k1 < p.kv_len ? acc1[r] * p.c : kNegInf;
+                for (int r = 0; r < 4; ++r) {
+                    s[r] = acc0[r] * p.c;
+                    s[4 + r] = acc1[r] * p.c;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int k0 = key0 + 4 * g + r, k1 = k0 + 16;
+                    s[r] = k0 <= qpos && k0 < p.kv_len ? acc0[r] * p.c : kNegInf;
+                    s[4 + r] = live1 && k1 <= qpos && k1 < p.kv_len ? acc1[r] * p.c : kNegInf;
+                }
             }
             float lmax = s[0];
 #pragma unroll
             for (int i = 1; i < 8; ++i) lmax = fmaxf(lmax, s[i]);
             const float tmax = group_max(lmax);
-            const float mn = fmaxf(m, tmax);
+            // The reference max m moves only when a score passes it by more
+            // than kLazy (log2 units), so p <= 2^kLazy and O is rescaled far
+            // less often; O and l share the reference, so O / l is the same
+            // up to rounding.
+            const bool grow = tmax > m + kLazy;   // m = -inf: any finite score
+            const float mn = grow ? tmax : m;
             const float ms = mn == kNegInf ? 0.f : mn;
-            const float alpha = fexp2(m - ms);
-            const bool grow = mn != m;
+            const float alpha = grow ? fexp2(m - ms) : 1.f;
             m = mn;
             float pr[8];
 #pragma unroll
