@@ -569,7 +569,16 @@ def main():
     c1.record(stream)
     torch.cuda.synchronize()
     copy_gbs = 2 * (1 << 30) * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9   # read + write
-    del src, dst
+    # and a plain 1 GiB read (torch's sum over int64: one pass, a few bytes out)
+    rd = src.view(torch.int64)
+    rd.sum()
+    c0.record(stream)
+    for _ in range(5):
+        rd.sum()
+    c1.record(stream)
+    torch.cuda.synchronize()
+    read_gbs = (1 << 30) * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst, rd
 
     value = ab["step"] / (ms_per_step * 1e-3) / 1e9
     # the dominant kernel: the fold (or the packed kernel); with one split it
@@ -606,6 +615,7 @@ def main():
         "warm_us_per_step": round(warm_ms * 1e3, 2),
         "step_us_percentiles": {"p10": pct(10), "p50": pct(50), "p90": pct(90)},
         "copy_1GiB_GBps": round(copy_gbs, 1),
+        "read_1GiB_GBps": round(read_gbs, 1),
         "kernels_us": {"splitk_fold": round(fold_avg * 1e3, 2),
                        "splitk_merge": round(merge_avg * 1e3, 2)},
         "roofline": {

@@ -102,3 +102,31 @@ def test_noalloc_refuses_a_workspace_past_its_scratch():
                                       D ** -0.5, 16) == P.PDA_OK
     torch.cuda.synchronize()
     assert not host_bits(out[:S - 1]).any()   # zero-length sequences give 0
+
+
+def test_noalloc_replays_in_a_hip_graph():
+    # the callers it is for include code under graph capture: the call
+    # captures (it launches kernels only) and every replay, with eager work
+    # and synchronisations between, gives the eager bytes
+    inp = W.make_paged("tiny", canary=True)
+    dev = PagedOnDevice(inp)
+    S, nq, D = inp.num_seqs, inp.num_q_heads, inp.head_dim
+    rc, want = _noalloc(dev, 4)
+    assert rc == P.PDA_OK
+    out = torch.zeros((S, nq, D), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        P.pda_paged_decode_noalloc(dev.q, dev.k, dev.v, dev.bt, dev.lens, out, S, nq,
+                                   inp.num_kv_heads, D, inp.block_size, dev.bt.shape[1],
+                                   inp.num_blocks, inp.scale, 4, stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"[noalloc graph] replay {r}")
+        assert np.array_equal(host_bits(out), host_bits(want))
+        _noalloc(dev, 16)   # eager use of the same scratch between replays
