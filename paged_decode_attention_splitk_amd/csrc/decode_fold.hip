@@ -228,6 +228,12 @@ __device__ __forceinline__ void seq_of_rank(const int32_t* __restrict__ lens, in
 #define PDA_FOLD_AUX 2
 #endif
 
+// P.V with P rounded to BF16 on token pairs (v_dot2, the default) or, with
+// 1, in FP32 FMAs (kept measurable: measured slower, with a smaller error).
+#ifndef PDA_FOLD_PV_FP32
+#define PDA_FOLD_PV_FP32 0
+#endif
+
 // Workgroups of at least this many waves merge each wave's token rows in
 // registers before the LDS merge (see the epilogue).
 constexpr int kRowMergeWaves = 4;
@@ -554,7 +560,35 @@ __global__ __launch_bounds__(fold_max_threads(GC)) void fold_kernel(const FoldPa
             }
         }
 
-        if constexpr (KV8) {
+        if constexpr (PDA_FOLD_PV_FP32) {
+            // P.V in FP32 (P not rounded): each token's V piece widened to
+            // FP32 (a BF16 pair is two shifts; E4M3 codes decode to BF16
+            // pairs first), one FMA per (head, dim, token)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                uint32_t vw[4];
+                if constexpr (KV8) {
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) {
+                        vw[2 * w] = fp8x2_to_bf16x2<false>(vr[u][w]);
+                        vw[2 * w + 1] = fp8x2_to_bf16x2<true>(vr[u][w]);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) vw[j] = vr[u][j];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v0 = __uint_as_float(vw[j] << 16);
+                    const float v1 = __uint_as_float(vw[j] & 0xFFFF0000u);
+#pragma unroll
+                    for (int h = 0; h < GC; ++h) {
+                        o[h][2 * j] = fmaf(pa[h * U + u], v0, o[h][2 * j]);
+                        o[h][2 * j + 1] = fmaf(pa[h * U + u], v1, o[h][2 * j + 1]);
+                    }
+                }
+            }
+        } else if constexpr (KV8) {
             // P.V on token pairs: the two tokens' codes of one dim are
             // interleaved (v_perm) and decoded to a BF16 pair, then v_dot2
             // with (p_u, p_u+1) rounded to BF16, accumulated in FP32 (fewer
