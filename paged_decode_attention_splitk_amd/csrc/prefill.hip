@@ -98,6 +98,8 @@ __device__ __forceinline__ int vchunk(int row, int chunk) {
     return row * kD + ((chunk ^ ((row & 7) << 2)) << 2);
 }
 
+// UNIFORM: the block size is a multiple of 16 (see the staging below).
+template <bool UNIFORM>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParams p) {
     extern __shared__ __align__(16) uint16_t smem[];   // 2 x (K tile, V tile)
     const int tid = threadIdx.x;
@@ -154,32 +156,60 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     // staging: thread t moves 16-byte pieces t + kThreads * i of the tile
     // (row = idx / 32, piece = idx % 32) for K and for V
     typedef u32x4_t Stage[2][kChunksPerThread];   // K, V pieces of one tile
-    // Table entries.  With a block size that is a multiple of 16, the 16
-    // rows a thread's piece i lies in (rows 16 i .. 16 i + 15 of the tile)
-    // sit in one block, since tiles start on a multiple of 32, so those
-    // entries are the same for the whole workgroup: they are read one tile
-    // ahead of the loads that use them (key kv_len - 1 stands in past the
-    // cache).  Other block sizes read each piece's entry with the tile's
+    // Table entries.  With a block size that is a multiple of 16 (UNIFORM),
+    // the 16 rows a thread's piece i lies in (rows 16 i .. 16 i + 15 of the
+    // tile) sit in one block, since tiles start on a multiple of 32, so
+    // those entries are the same for the whole workgroup: they are read one
+    // tile ahead of the loads that use them (key kv_len - 1 stands in past
+    // the cache), and a piece's address is a workgroup-uniform base plus the
+    // thread's constant byte offset, so staging a tile costs no vector
+    // arithmetic.  Other block sizes read each piece's entry with the tile's
     // loads, every table read of the tile first, with no branch between
     // them, so they are waited for once.
     static_assert(kThreads == 512 && kChunksPerThread == 2, "piece i covers rows 16 i .. 16 i + 15");
-    const bool uniform_tbl = p.bs % 16 == 0;
     auto tbl_half = [&](int tile, int i) {
-        return uniform_tbl ? p.table[min(tile * kKT + 16 * i, p.kv_len - 1) / p.bs] : 0;
+        return UNIFORM ? p.table[min(tile * kKT + 16 * i, p.kv_len - 1) / p.bs] : 0;
     };
     const int b0 = p.table[0];
+    // the thread's bytes inside its 16-row run: row tid / 32, piece tid % 32
+    const uint32_t lane_b = (uint32_t)(((tid >> 5) * p.tok_s + (tid & 31) * 8) * 2);
     auto stage_load = [&](int tile, Stage& st, const int (&bt)[2]) {
-        int jr[kChunksPerThread], bj[kChunksPerThread];
+        if constexpr (UNIFORM) {
 #pragma unroll
-        for (int i = 0; i < kChunksPerThread; ++i) {
-            jr[i] = tile * kKT + ((tid + kThreads * i) >> 5);
-            bj[i] = uniform_tbl ? bt[i] : p.table[(jr[i] < p.kv_len ? jr[i] : 0) / p.bs];
-        }
+            for (int i = 0; i < kChunksPerThread; ++i) {
+                // a block outside the pool inside the cache (unspecified
+                // result) reads rows of the first block instead
+                const int j0 = tile * kKT + 16 * i;
+                const bool ok = (uint32_t)bt[i] < p.num_blocks;
+                const int blk = ok ? bt[i] : ((uint32_t)b0 < p.num_blocks ? b0 : 0);
+                const int64_t ub =
+                    ((int64_t)blk * p.blk_s + (int64_t)(ok ? j0 % p.bs : 0) * p.tok_s) * 2;
+                st[0][i] = *reinterpret_cast<const u32x4_t*>(
+                    reinterpret_cast<const char*>(kbase) + ub + lane_b);
+                st[1][i] = *reinterpret_cast<const u32x4_t*>(
+                    reinterpret_cast<const char*>(vbase) + ub + lane_b);
+            }
+            if (tile * kKT + kKT > p.kv_len) {
+                // rows past the cache (read from inside the last block) are
+                // zeroed: their scores are masked and p = 0 meets 0
 #pragma unroll
-        for (int i = 0; i < kChunksPerThread; ++i) {
-            const int64_t off = key_row(jr[i], bj[i], b0) + ((tid + kThreads * i) & 31) * 8;
-            st[0][i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
-            st[1][i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+                for (int i = 0; i < kChunksPerThread; ++i)
+                    if (tile * kKT + 16 * i + (tid >> 5) >= p.kv_len)
+                        st[0][i] = st[1][i] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+        } else {
+            int jr[kChunksPerThread], bj[kChunksPerThread];
+#pragma unroll
+            for (int i = 0; i < kChunksPerThread; ++i) {
+                jr[i] = tile * kKT + ((tid + kThreads * i) >> 5);
+                bj[i] = p.table[(jr[i] < p.kv_len ? jr[i] : 0) / p.bs];
+            }
+#pragma unroll
+            for (int i = 0; i < kChunksPerThread; ++i) {
+                const int64_t off = key_row(jr[i], bj[i], b0) + ((tid + kThreads * i) & 31) * 8;
+                st[0][i] = *reinterpret_cast<const u32x4_t*>(kbase + off);
+                st[1][i] = *reinterpret_cast<const u32x4_t*>(vbase + off);
+            }
         }
     };
     auto stage_store = [&](int buf, const Stage& st) {
@@ -370,18 +400,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     const size_t lds = sizeof(uint16_t) * 4 * (size_t)kTileElems;   // 2 x (K, V) tiles
-    if (lds > 64 * 1024) {
-        static bool granted = false;   // racy first calls only repeat the request
-        if (!granted) {
-            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_kernel),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)lds);
-            if (e != hipSuccess) return e;
-            granted = true;
-        }
-    }
+    static_assert(sizeof(uint16_t) * 4 * (size_t)kTileElems <= 64 * 1024,
+                  "the staged tiles fit the default LDS limit of a workgroup");
     const dim3 grid((uint32_t)p.nq, (uint32_t)((p.q_len + kRows - 1) / kRows));
-    hipLaunchKernelGGL(prefill_kernel, grid, dim3(kThreads), lds, stream, p);
+    if (p.bs % 16 == 0)
+        hipLaunchKernelGGL(prefill_kernel<true>, grid, dim3(kThreads), lds, stream, p);
+    else
+        hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(kThreads), lds, stream, p);
     return hipGetLastError();
 }
 
