@@ -360,6 +360,8 @@ def prefill_bench(args, K):
     flops = 4.0 * nq * D * float(keys.sum())
     tflops = flops / (gpu_ms * 1e-3) / 1e12
     kv_bytes = pi.kv_len * nkv * D * 2 * 2
+    # block sizes that are multiples of 16 take the uniform-staging instance
+    kname = f"prefill_kernel<{'true' if bs % 16 == 0 else 'false'}>"
     return {
         "metric": "causal paged prefill TFLOP/s", "value": round(flops / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -369,11 +371,11 @@ def prefill_bench(args, K):
                    "q_offset": pi.q_offset, "num_q_heads": nq, "num_kv_heads": nkv,
                    "head_dim": D, "block_size": bs, "flops_per_step": flops},
         "us_per_step": round(ms * 1e3, 2), "gpu_event_us_per_step": round(gpu_ms * 1e3, 2),
-        "roofline": {"kernel": "causal prefill (prefill_kernel)", "bound": "mfma",
+        "roofline": {"kernel": f"causal prefill ({kname})", "bound": "mfma",
                      "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4),
                      "traffic": load_traffic("prefill_4096" if args.workload == "prefill"
-                                             else args.workload, "prefill_kernel"),
+                                             else args.workload, kname),
                      "kv_bytes_per_step": kv_bytes},
     }
 
