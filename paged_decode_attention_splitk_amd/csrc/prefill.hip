@@ -324,21 +324,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
             float lmax = s[0];
 #pragma unroll
             for (int i = 1; i < 8; ++i) lmax = fmaxf(lmax, s[i]);
-            const float tmax = group_max(lmax);
             // The reference max m moves only when a score passes it by more
             // than kLazy (log2 units), so p <= 2^kLazy and O is rescaled far
             // less often; O and l share the reference, so O / l is the same
-            // up to rounding.
-            const bool grow = tmax > m + kLazy;   // m = -inf: any finite score
-            const float mn = grow ? tmax : m;
-            const float ms = mn == kNegInf ? 0.f : mn;
-            const float alpha = grow ? fexp2(m - ms) : 1.f;
-            m = mn;
+            // up to rounding.  The max over the four lane groups is taken
+            // only when some lane's own scores pass the slack.
+            bool grow = false;   // m = -inf: any finite score grows it
+            float alpha = 1.f;
+            if (__builtin_amdgcn_ballot_w64(lmax > m + kLazy) != 0) {
+                const float tmax = group_max(lmax);
+                grow = tmax > m + kLazy;
+                if (grow) {
+                    alpha = m == kNegInf ? 0.f : fexp2(m - tmax);
+                    m = tmax;
+                }
+            }
+            const float ms = m == kNegInf ? 0.f : m;
             float pr[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) pr[i] = fexp2(s[i] - ms);
-            l = l * alpha +
-                group_sum(((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+            // this lane's part of l (its own keys of the tile); the four
+            // groups' parts are added once, after the last tile
+            l = l * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
             // P as the A operand of a 32-key step: lane = query c, k index
             // 8g + t = key 4g + t of block 0 (t < 4) or of block 1 (t >= 4)
             const u32x4_t pw = {pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
@@ -380,6 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     }
 
     // out = O / l (0 where l is 0), rows 4g + r of this wave
+    l = group_sum(l);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const float L =
