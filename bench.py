@@ -524,9 +524,12 @@ def main():
 
     K = args.steps
 
+    enqueue_ms = [0.0]
+
     def timed(fn):
         """Average ms of fn(i) over K calls, from HIP events on the launch
-        stream around the whole run, and the host wall clock of the run."""
+        stream around the whole run, and the host wall clock of the run
+        (the host's own time to issue the K calls is kept in enqueue_ms)."""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -534,6 +537,7 @@ def main():
         e0.record(stream)
         for i in range(K):
             fn(i)
+        enqueue_ms[0] = (time.perf_counter() - t0) * 1e3 / K
         e1.record(stream)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / K
@@ -541,6 +545,7 @@ def main():
 
     # the timed region: K whole decode steps through pda_paged_decode
     gpu_ms, ms_per_step = timed(decode)
+    host_enqueue_ms = enqueue_ms[0]
     # each kernel on its own, back to back, for its average duration
     fold_avg, _ = timed(partials)
     merge_avg, _ = timed(lambda i: merge())
@@ -614,6 +619,9 @@ def main():
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "gpu_event_us_per_step": round(gpu_ms * 1e3, 2),
+        # the host's time to issue one step (binding + two launches): well
+        # under the step, so the timed loop is bound by the GPU, not the host
+        "host_enqueue_us_per_step": round(host_enqueue_ms * 1e3, 2),
         "warm_us_per_step": round(warm_ms * 1e3, 2),
         "step_us_percentiles": {"p10": pct(10), "p50": pct(50), "p90": pct(90)},
         "copy_1GiB_GBps": round(copy_gbs, 1),
