@@ -395,7 +395,9 @@ int partials_impl(const DecodeShape& s, const void* q, const void* k, const void
 // launch (its parts form; 1 = one workgroup each, the pages' launch shape).
 // Measured on 64 sequences of 1K-8K tokens (32 q / 4 kv heads, D 256):
 // 1 part 253 us, 2 parts of 8 waves 213 us (all 512 workgroups resident at
-// once, two per CU), 4 of 4 waves 221 us, 8 parts 280 us and more.
+// once, two per CU), 4 of 4 waves 221 us, 8 parts 280 us and more; again
+// with the kernel's non-temporal K/V loads: 2 of 8 waves 204.7 us, 3 of 4
+// 209.0, 3 of 8 210.9, 4 of 4 216.7, 2 of 4 242.6.
 #ifndef PDA_PACKED_PARTS
 #define PDA_PACKED_PARTS 2
 #endif
