@@ -1,6 +1,7 @@
-"""The decode calls inside a captured HIP graph (torch.cuda.CUDAGraph on the
-library's stream argument): every replay, with eager work and
-synchronisations between replays, gives the eager bytes.  Needs an MI355X."""
+"""The decode calls, the tiled step and the causal prefill inside a captured
+HIP graph (torch.cuda.CUDAGraph on the library's stream argument): every
+replay, with eager work and synchronisations between replays, gives the
+eager bytes.  Needs an MI355X."""
 import numpy as np
 import pytest
 
@@ -8,8 +9,10 @@ torch = pytest.importorskip("torch")
 
 pytestmark = pytest.mark.gpu
 
+import dataclasses
+
 import workloads as W
-from tests.gpu_util import PagedOnDevice, ScratchOnDevice, dev_i32, host_bits, say
+from tests.gpu_util import PagedOnDevice, ScratchOnDevice, dev_i32, dev_u16, host_bits, say
 
 import paged_decode_attention_splitk_amd as P
 
@@ -115,3 +118,36 @@ def test_tiled_step_graph_replays():
         step()
         torch.cuda.synchronize()
     h.close()
+
+
+# the causal prefill (a kernel launch only): both staging forms, block size
+# 16 (uniform block base per 16-row piece) and 8 (per-row table reads)
+@pytest.mark.parametrize("bs", [16, 8])
+def test_prefill_graph_replays(bs):
+    w = dataclasses.replace(W.WORKLOADS["prefill"], seed=33, num_q_heads=16, num_kv_heads=2,
+                            block_size=bs)
+    pi = W.make_prefill(w, canary=True, q_len=300, kv_len=1000, q_offset=700)
+    q, k, v = dev_u16(pi.q), dev_u16(pi.k_cache), dev_u16(pi.v_cache)
+    bt = dev_i32(pi.block_table)
+    out = torch.empty((pi.q_len, pi.num_q_heads, pi.head_dim), dtype=torch.bfloat16,
+                      device="cuda")
+    say(f"[graph prefill] bs={bs}")
+
+    def call():
+        P.pda_paged_prefill(q, k, v, out, bt, pi.q_len, pi.kv_len, pi.q_offset,
+                            pi.num_q_heads, pi.num_kv_heads, pi.head_dim, pi.block_size,
+                            len(pi.block_table), pi.num_blocks, pi.scale)
+
+    call()
+    torch.cuda.synchronize()
+    eager = host_bits(out).copy()
+    g = _capture(call)
+    for r in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out), eager), f"replay {r} differs"
+        call()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out), eager)
