@@ -221,7 +221,9 @@ hipError_t launch_oneshot(int mode, const DecodeShape& s, int gc, int hg, pda::F
 // sequence runs one workgroup each, with no hand-over.  Measured on 128
 // sequences of 0-16K tokens, 64-block tiles: 1 part 1134 us per step, 2
 // parts 1103, 3 parts 1079, 4 parts 1100 (each part workgroup in the grid
-// costs the partial-block calls dispatch time).
+// costs the partial-block calls dispatch time).  Again with the balanced
+// tile plan and the partial-block calls at one part: 3 parts 1058 us, 4
+// parts 1055, 2 parts 1099; 12 waves 1164; 4 parts of 6 waves 1134.
 #ifndef PDA_TILED_PARTS
 #define PDA_TILED_PARTS 3
 #endif
