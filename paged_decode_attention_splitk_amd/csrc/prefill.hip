@@ -141,7 +141,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(const PrefillParam
     f32x4_t O[16];   // O[query 4g + r][dim 16 nb + c]
 #pragma unroll
     for (int nb = 0; nb < 16; ++nb) O[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m = kNegInf, l = 0.f;   // of query c (same in all four groups)
+    // m: the reference max of query c (the same in all four lane groups);
+    // l: this lane's part of query c's sum, the groups' parts added at the end
+    float m = kNegInf, l = 0.f;
 
     const uint16_t* kbase = p.k + (int64_t)kvh * kD;
     const uint16_t* vbase = p.v + (int64_t)kvh * kD;
